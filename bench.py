@@ -1,0 +1,308 @@
+"""Benchmark of the node-local data path of TIDE's layout-aware FSDP2
+collectives on one MI355X.
+
+One step = the whole hot path over one layer of synthetic gradients:
+all-gather placement of the rank-major bf16 gathered buffer into the
+per-parameter tensors, then the fused reduce-scatter of R ranks' bf16
+gradients into fp32 dim-0 shards (the plan is built once per layer, before
+timing, as in training).  Inputs are resident in HBM before the timed
+region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--probe]
+
+Metric (bytes are algorithmic): RS GB/s = (R*N*2 + N*4) / t_RS and its
+fraction of the 8 TB/s HBM peak; AG GB/s = 4*N / t_AG; GEMM slowdown of a
+single-wave bf16 GEMM running beside the RS (with --probe).  ``value`` is
+the whole step's algorithmic bytes over the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(HERE, "profiles")
+RS_SOURCES = ["shard_placement_amd/csrc/rs.hip", "shard_placement_amd/csrc/plan_format.h"]
+AG_SOURCES = ["shard_placement_amd/csrc/ag.hip", "shard_placement_amd/csrc/plan_format.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(HERE, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, sources) -> dict:
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "%s_%s_pmc.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha256_16") != src_hash(sources):
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(st, budget_s: float):
+    """Time the CPU oracle (all host threads) on a bounded sample of the same
+    workload: whole params in order until about budget_s of oracle time.  The
+    GPU's shards of those params are compared bit for bit on the way."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    w = st.w
+    _, m, off, _ = oracle.layout(w.shapes, w.R)
+    used, nbytes, t_total, t_d2h, mism = [], 0, 0.0, 0.0, 0
+    for p, shp in enumerate(w.shapes):
+        n = 1
+        for d in shp:
+            n *= d
+        t0 = time.perf_counter()
+        g = [[st.grads[q][p].reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)]
+             for q in range(w.R)]
+        got = [st.out[r][int(off[p]):int(off[p]) + int(m[p])].view(torch.int32).cpu().numpy()
+               for r in range(w.R)]
+        t_d2h += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        want = oracle.rs([shp], w.R, g)
+        t_total += time.perf_counter() - t0
+        for r in range(w.R):
+            mism += int(np.count_nonzero(got[r].view(np.uint32) != want[r][:int(m[p])].view(np.uint32)))
+        used.append(w.names[p])
+        nbytes += w.R * n * 2 + n * 4
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(nbytes / t_total / 1e9, 3), "unit": "GB/s",
+        "cores": oracle.max_threads(), "kind": "oracle",
+        "sample": "reduce-scatter of params %s of %s (R=%d, %.2f GB algorithmic, "
+                  "%.1f s oracle time; device->host copy %.1f s not counted); GPU shards "
+                  "of these params bit-exact: %s" % (
+                      ",".join(used), w.name, w.R, nbytes / 1e9, t_total, t_d2h,
+                      "yes" if mism == 0 else "NO (%d words differ)" % mism),
+        "parity_mismatches": mism,
+    }
+
+
+def gemm_probe(st, iters: int = 50):
+    """Single-wave bf16 GEMM alone and beside the reduce-scatter.  Returns a
+    dict of times and the slowdown; the GEMM runs on a second stream."""
+    import torch
+
+    M, N, K = 4096, 4096, 8192
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def gemm_times(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        with torch.cuda.stream(side):
+            for e0, e1 in evs:
+                e0.record()
+                torch.matmul(a, b, out=c)
+                e1.record()
+        return evs
+
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    alone = gemm_times(iters)
+    torch.cuda.synchronize()
+    t0 = sorted(e0.elapsed_time(e1) for e0, e1 in alone)[iters // 2]
+    # concurrent: a train of reduce-scatters on the main stream, GEMMs beside it
+    rs0 = torch.cuda.Event(enable_timing=True)
+    rs1 = torch.cuda.Event(enable_timing=True)
+    n_rs = max(1, int(iters * t0 / 3.0) + 2)
+    rs0.record(main)
+    for _ in range(n_rs):
+        st.plan.rs(stream=main)
+    rs1.record(main)
+    side.wait_event(rs0)
+    conc = gemm_times(iters)
+    torch.cuda.synchronize()
+    inside = []
+    rs_start = 0.0
+    rs_end = rs0.elapsed_time(rs1)
+    for e0, e1 in conc:
+        s = rs0.elapsed_time(e0)
+        e = rs0.elapsed_time(e1)
+        if rs_start <= s and e <= rs_end:
+            inside.append(e0.elapsed_time(e1))
+    t1 = sorted(inside)[len(inside) // 2] if inside else None
+    return {"gemm": "bf16 %dx%dx%d torch.matmul" % (M, N, K), "t_alone_ms": round(t0, 4),
+            "t_concurrent_ms": round(t1, 4) if t1 else None, "n_inside": len(inside),
+            "rs_launches": n_rs,
+            "slowdown_pct": round(100.0 * (t1 / t0 - 1.0), 2) if t1 else None}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="2", help="workload key or name (default: the Llama-3.1-70B layer, R=8)")
+    ap.add_argument("--flags", type=int, default=-1, help="TIDE_FLAG_* access hints (-1: default)")
+    ap.add_argument("--rs-tile", type=int, default=0)
+    ap.add_argument("--ag-tile", type=int, default=0)
+    ap.add_argument("--max-wg", type=int, default=0, help="cap the RS grid (0: one workgroup per tile)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="run the concurrent-GEMM interference probe")
+    ap.add_argument("--no-sdma", action="store_true", help="skip timing the copy-engine placement")
+    ap.add_argument("--calib-copy-mib", type=int, default=1024,
+                    help="size of a plain device copy run once (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(all R simulated ranks live in one GPU's HBM); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from shard_placement_amd import configs, harness
+
+    if not torch.cuda.is_available():
+        print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
+        sys.exit(1)
+    w = configs.get(args.workload)
+    log("workload", w.name, "R", w.R, "P", w.P, "N", w.numel())
+    t0 = time.perf_counter()
+    st = harness.setup(w, guard=0, flags=args.flags, rs_tile=args.rs_tile, ag_tile=args.ag_tile)
+    torch.cuda.synchronize()
+    log("setup %.1f s; plan: %d RS tiles of %d, %d AG tiles of %d, blob %d B" % (
+        time.perf_counter() - t0, st.plan.info.rs_tiles, st.plan.info.rs_tile_elems,
+        st.plan.info.ag_tiles, st.plan.info.ag_tile_elems, st.plan.info.blob_bytes))
+
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 19, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    rsb, agb = harness.rs_bytes(w), harness.ag_bytes(w)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        st.plan.ag()
+        if ev:
+            ev[1].record()
+        st.plan.rs(max_workgroups=args.max_wg)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ag_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    rs_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+    rs_avg = sum(rs_ms) / len(rs_ms)
+    ag_avg = sum(ag_ms) / len(ag_ms)
+    rs_gbs = rsb / (rs_avg * 1e-3) / 1e9
+    ag_gbs = agb / (ag_avg * 1e-3) / 1e9
+    log("step %.3f ms; RS avg %.3f ms (min %.3f) = %.0f GB/s; AG avg %.3f ms = %.0f GB/s" % (
+        ms_step, rs_avg, min(rs_ms), rs_gbs, ag_avg, ag_gbs))
+
+    sdma = None
+    if not args.no_sdma:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.plan.ag_sdma()
+        torch.cuda.synchronize()
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            st.plan.ag_sdma()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps
+        sdma = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
+                "engine": "hipMemcpyDeviceToDeviceNoCU copies (2-D per param + 1-D partial rank)"}
+        log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
+
+    probe = gemm_probe(st) if args.probe else None
+    if probe:
+        log("probe", probe)
+
+    traffic = read_traffic("rs", w.name, RS_SOURCES)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host cores")
+        cpu = cpu_baseline(st, args.cpu_budget)
+        log("cpu baseline", cpu)
+
+    rec = {
+        "metric": "RS bf16->fp32 shard GB/s & % of HBM peak; AG placement GB/s; GEMM slowdown %",
+        "value": round((rsb + agb) / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded bf16 N(0,%g) gradients shaped like %s" % (w.sigma, w.name),
+        "config": {"workload": w.name, "R": w.R, "P": w.P, "N": w.numel(),
+                   "step": "AG placement + fused RS", "slot_reuse": w.slot_reuse,
+                   "rs_bytes": rsb, "ag_bytes": agb},
+        "rs_gbps": round(rs_gbs, 1),
+        "rs_frac_hbm": round(rs_gbs / HBM_PEAK_GBS, 4),
+        "rs_ms": round(rs_avg, 4),
+        "ag_gbps": round(ag_gbs, 1),
+        "ag_frac_hbm": round(ag_gbs / HBM_PEAK_GBS, 4),
+        "ag_ms": round(ag_avg, 4),
+        "ag_sdma": sdma,
+        "gemm_slowdown_pct": probe["slowdown_pct"] if probe else None,
+        "probe": probe,
+        "roofline": {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(rs_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "rs_fixed_kernel",
+                     "algorithmic_bytes_per_launch": rsb},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    if cpu and cpu.get("parity_mismatches"):
+        sys.exit(3)
+
+
+if __name__ == "__main__":
+    main()

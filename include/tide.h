@@ -1,0 +1,195 @@
+/*
+ * tide.h -- C ABI of libtide: the node-local data path of TIDE's
+ * layout-aware FSDP2 collectives on one MI355X (gfx950).
+ *
+ * Sources, cited by page and section:
+ *   [Abstract]  "The Endgame of FSDP Communication: Layout-Aware Collectives
+ *               on Copy Engines, RDMA, and NVSwitch" (weekinpapers.com),
+ *               section Abstract.
+ *   [Root]      kongchang.com article "The Endgame of FSDP Communication:
+ *               TIDE Zero-Copy Collective Communication Optimization",
+ *               section "The Root of FSDP2 Communication Overhead".
+ *   [Design]    same article, section "TIDE's Design Approach".
+ *
+ * FSDP2 keeps gradients and parameters as per-parameter tensors while its
+ * collectives use flat rank-major buffers; TIDE folds the placement into
+ * the collectives' addressing [Abstract; Root].  This library does that for
+ * R simulated ranks whose buffers all sit in one GPU's HBM:
+ *
+ *   reduce-scatter  R ranks' per-parameter bf16 gradients, read in place,
+ *                   are reduced into each rank's fp32 dim-0 shards
+ *                   [Abstract: "consumes per-parameter bf16 gradients
+ *                   directly and reduces them into fp32 shards"];
+ *   AG placement    a rank-major bf16 gathered buffer [Root] is written
+ *                   straight into the per-parameter full tensors, the
+ *                   padding rows trimmed [Abstract: TIDE-AG "delivers shards
+ *                   directly to parameter storage"].
+ *
+ * Layout conventions (the pages leave them open; these readings are the
+ * library's contract):
+ *   - A parameter of shape [d0, rest...] is d0 rows of c = prod(rest)
+ *     elements (c = 1 for 1-D; a 0-d parameter is passed as {1, 1}).
+ *   - Rank r owns rows [r*s, r*s + s), s = ceil(d0 / R) ("chunk rows");
+ *     rows >= d0 are padding.  Shard numel m = s*c.
+ *   - Rank r's fp32 arena holds param p's shard at element offset off[p] =
+ *     sum over p' < p of round_up(m[p'], align_elems); slot numel S is the
+ *     offset after the last param.  A bf16 gathered slot uses the same
+ *     offsets; the gathered buffer is R slots, slot r at element r*S.
+ *   - Shard element i of rank r for param p is the sum over ranks of flat
+ *     gradient element j = r*m + i when j < d0*c, else +0.0f (padding).
+ *     The sum is fp32, in rank order 0..R-1 starting from rank 0's value
+ *     (order 0), or pairwise over adjacent ranks level by level with an odd
+ *     last element carried up (order 1); each add is one IEEE binary32
+ *     round-to-nearest-even add, subnormals kept.
+ *
+ * Memory and ownership: the caller owns every buffer, including the plan
+ * blob (host) and its device copy.  The library allocates no device memory,
+ * keeps no state between calls and never synchronises a stream; launches
+ * are asynchronous on the caller's stream.  A plan holds raw device
+ * addresses: it is invalid once any of them is freed.
+ *
+ * Errors: every entry point returns a tide_status; nothing is thrown
+ * across the ABI and no launch is made when validation fails.  Faults
+ * during execution surface at the caller's next synchronisation.
+ */
+#ifndef TIDE_H
+#define TIDE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TIDE_ABI_VERSION 1
+
+/* A hipStream_t (struct ihipStream_t*); NULL is the null stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t *tide_stream_t;
+
+typedef enum tide_status {
+    TIDE_OK = 0,
+    TIDE_EINVAL = -1,       /* bad argument: NULL, R < 1, negative size, ... */
+    TIDE_EALIGN = -2,       /* a pointer is not aligned to its element size */
+    TIDE_EOVERLAP = -3,     /* an output range overlaps an input or output */
+    TIDE_ENOSPACE = -4,     /* plan blob too small (needed size reported) */
+    TIDE_EHIP = -5,         /* the HIP runtime refused a launch or copy */
+    TIDE_EUNSUPPORTED = -6, /* valid request this plan cannot serve */
+    TIDE_EPLAN = -7         /* not a plan blob, or wrong version */
+} tide_status;
+
+/* One parameter: d0 rows of row_numel elements (0-d => {1, 1}). */
+typedef struct tide_shape {
+    int64_t dim0;
+    int64_t row_numel;
+} tide_shape;
+
+/* Plan options; pass NULL for the defaults. */
+typedef struct tide_opts {
+    int64_t align_elems;   /* arena/slot offset alignment, elements (>= 1; default 1) */
+    int32_t rs_tile_elems; /* elements per reduce-scatter tile, multiple of 2048
+                              (0: chosen from R) */
+    int32_t ag_tile_elems; /* elements per placement tile, multiple of 2048 (0: 16384) */
+    int32_t flags;         /* -1: library default; else an OR of TIDE_FLAG_* */
+    int32_t reserved;      /* must be 0 */
+} tide_opts;
+
+/* Access hints (results are identical with any combination). */
+#define TIDE_FLAG_NT_LOADS  1  /* streaming (non-temporal) source loads */
+#define TIDE_FLAG_NT_STORES 2  /* streaming (non-temporal) destination stores */
+
+/* What a built plan holds (filled by tide_desc_build / tide_plan_query). */
+typedef struct tide_plan_info {
+    int32_t R, P;
+    int64_t slot_numel;     /* S */
+    int64_t numel;          /* N = sum of d0*c */
+    int64_t padded_numel;   /* R*S minus alignment gaps = sum of R*m */
+    int64_t rs_tiles;       /* 0 when the plan has no reduce-scatter pointers */
+    int64_t ag_tiles;       /* 0 when the plan has no placement pointers */
+    int32_t rs_tile_elems, ag_tile_elems;
+    int64_t blob_bytes;     /* bytes of the blob in use: upload this many */
+} tide_plan_info;
+
+/* Size of the plan blob for these shapes (an upper bound that holds for
+ * any pointers).  shapes: P entries, host memory.  [Abstract: layout
+ * placement folded into collective addressing] */
+tide_status tide_desc_size(const tide_shape *shapes, int32_t P, int32_t R,
+                           const tide_opts *opts, size_t *blob_bytes);
+
+/* Shard geometry without pointers (host only): per param the chunk rows
+ * s = ceil(d0/R), shard numel m = s*c and arena/slot offset off; and the
+ * slot numel S, so that a caller can size the fp32 arenas (S floats per
+ * rank) and the gathered buffer (R*S bf16) before building a plan.  Each
+ * output array has P entries (host memory) and may be NULL; slot_numel
+ * must not be NULL. */
+tide_status tide_desc_geometry(const tide_shape *shapes, int32_t P, int32_t R,
+                               const tide_opts *opts, int64_t *chunk_rows,
+                               int64_t *shard_numel, int64_t *offsets,
+                               int64_t *slot_numel);
+
+/* Build a plan (descriptor table) into caller host memory `blob`.
+ *   grads     [R*P] device addresses, rank-major: grads[q*P + p] is rank q's
+ *             bf16 gradient of param p (d0*c contiguous elements), or NULL
+ *             for a plan without reduce-scatter;
+ *   out_base  [R] device addresses of each rank's fp32 arena (>= S floats),
+ *             NULL together with grads;
+ *   gathered  device address of the bf16 gathered buffer (R*S elements), or
+ *             NULL for a plan without placement;
+ *   full      [P] device addresses of the bf16 full tensors (d0*c each),
+ *             NULL together with gathered.
+ * Pointer arrays are host memory and are read, not kept.  Validates
+ * element alignment (2 B for bf16, 4 B for fp32) and that no reduce-scatter
+ * output overlaps a gradient or another output, and no placement output
+ * overlaps the gathered buffer or another output.  Reduce-scatter outputs
+ * MAY overlap the gathered buffer (Slot-Reuse: shards staged in vacated
+ * all-gather memory [Abstract; Design]).  Zero-sized params need no
+ * pointer.  On TIDE_ENOSPACE, info->blob_bytes (if info) holds the size
+ * needed.  info may be NULL.  [Abstract; Root] */
+tide_status tide_desc_build(const tide_shape *shapes, int32_t P, int32_t R,
+                            const tide_opts *opts, const void *const *grads,
+                            void *const *out_base, const void *gathered,
+                            void *const *full, void *blob, size_t blob_bytes,
+                            tide_plan_info *info);
+
+/* Read back what a host plan blob holds. */
+tide_status tide_plan_query(const void *h_plan, tide_plan_info *info);
+
+/* Fused reduce-scatter [Abstract: TIDE-RS; Root: each rank ends with the
+ * reduction of its own shard].  h_plan: the host blob; d_plan: its device
+ * copy (first info.blob_bytes bytes, 16-byte aligned), both unchanged
+ * since the build.  order: 0 fixed rank order, 1 pairwise tree.
+ * max_workgroups: 0 launches one short-lived workgroup per tile; n > 0
+ * caps the grid at n workgroups that stride over the tiles.  Asynchronous
+ * on `stream`; allocates nothing. */
+tide_status tide_rs_bf16_to_fp32(const void *h_plan, const void *d_plan,
+                                 int32_t order, int32_t max_workgroups,
+                                 tide_stream_t stream);
+
+/* All-gather placement on the compute units [Abstract: TIDE-AG]: for
+ * every param p and rank r, the clamp(d0 - r*s, 0, s) valid rows of slot r
+ * are copied to rows [r*s, ...) of full[p]; slot padding is never read.
+ * Arguments as for tide_rs_bf16_to_fp32. */
+tide_status tide_ag_place(const void *h_plan, const void *d_plan,
+                          int32_t max_workgroups, tide_stream_t stream);
+
+/* The same placement issued as copies on the DMA (copy) engines, with no
+ * compute-unit kernel [Abstract: no SMs used for placement]: at most two
+ * copies per param (a 2-D copy over the ranks with full shards, a 1-D copy
+ * for the one partial rank), issued from the host plan, asynchronous on
+ * `stream`.  engine_only = 1 requests the runtime's no-compute-unit copy
+ * kind; 0 lets the runtime choose. */
+tide_status tide_ag_place_sdma(const void *h_plan, int32_t engine_only,
+                               tide_stream_t stream);
+
+/* Static text for a status code. */
+const char *tide_status_str(int32_t status);
+
+/* TIDE_ABI_VERSION of the loaded library. */
+int32_t tide_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDE_H */

@@ -1,0 +1,214 @@
+"""Python binding of libtide: argument marshalling only.
+
+Functions carry the C ABI's names (include/tide.h) and pass torch tensors'
+device addresses and the current HIP stream straight through; every step of
+the data path runs in the library's HIP kernels (or, for
+``tide_ag_place_sdma``, on the DMA engines).  ``Plan`` bundles one layer's
+descriptor table (host blob + its device copy) with the tensors it points
+at, so that they outlive it.
+
+Operations (Abstract of "The Endgame of FSDP Communication",
+weekinpapers.com): the reduce-scatter reads R ranks' per-parameter bf16
+gradients in place and writes each rank's fp32 dim-0 shards; the placement
+writes a rank-major bf16 gathered buffer into per-parameter tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import TideError, TideOpts, TidePlanInfo, TideShape, check
+
+ORDERS = {"fixed": 0, "tree": 1}
+
+
+def _shapes(shapes: Sequence[Sequence[int]]):
+    arr = (TideShape * max(1, len(shapes)))()
+    for i, shp in enumerate(shapes):
+        shp = tuple(int(x) for x in shp)
+        if len(shp) == 0:
+            arr[i].dim0, arr[i].row_numel = 1, 1
+        else:
+            c = 1
+            for d in shp[1:]:
+                c *= d
+            arr[i].dim0, arr[i].row_numel = shp[0], c
+    return arr
+
+
+def _opts(align: int = 1, rs_tile: int = 0, ag_tile: int = 0, flags: int = -1) -> TideOpts:
+    return TideOpts(int(align), int(rs_tile), int(ag_tile), int(flags), 0)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def tide_desc_geometry(shapes, R: int, align: int = 1) -> Tuple[np.ndarray, np.ndarray, np.ndarray, int]:
+    """(chunk rows, shard numel, offsets, slot numel S) from the library."""
+    L = _lib.lib()
+    P = len(shapes)
+    s = np.zeros(max(1, P), np.int64)
+    m = np.zeros(max(1, P), np.int64)
+    off = np.zeros(max(1, P), np.int64)
+    S = ctypes.c_int64(0)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    o = _opts(align)
+    check(L.tide_desc_geometry(_shapes(shapes), P, int(R), ctypes.byref(o),
+                               s.ctypes.data_as(i64p), m.ctypes.data_as(i64p),
+                               off.ctypes.data_as(i64p), ctypes.byref(S)), "tide_desc_geometry")
+    return s[:P], m[:P], off[:P], int(S.value)
+
+
+def tide_desc_size(shapes, R: int, align: int = 1, rs_tile: int = 0, ag_tile: int = 0,
+                   flags: int = -1) -> int:
+    n = ctypes.c_size_t(0)
+    o = _opts(align, rs_tile, ag_tile, flags)
+    check(_lib.lib().tide_desc_size(_shapes(shapes), len(shapes), int(R), ctypes.byref(o),
+                                    ctypes.byref(n)), "tide_desc_size")
+    return int(n.value)
+
+
+def tide_desc_build(shapes, R: int, grad_ptrs=None, out_ptrs=None, gathered_ptr=None,
+                    full_ptrs=None, align: int = 1, rs_tile: int = 0, ag_tile: int = 0,
+                    flags: int = -1) -> Tuple[np.ndarray, TidePlanInfo]:
+    """Build a host plan blob from raw device addresses (ints).  grad_ptrs is
+    rank-major [R*P]; out_ptrs [R]; full_ptrs [P].  Returns (blob, info)."""
+    L = _lib.lib()
+    P = len(shapes)
+    size = tide_desc_size(shapes, R, align, rs_tile, ag_tile, flags)
+    blob = np.zeros(size, np.uint8)
+    vp = ctypes.c_void_p
+
+    def arr(ptrs, n):
+        if ptrs is None:
+            return None
+        a = (vp * max(1, n))()
+        for i, x in enumerate(ptrs):
+            a[i] = int(x) if x else None
+        return a
+
+    info = TidePlanInfo()
+    o = _opts(align, rs_tile, ag_tile, flags)
+    st = L.tide_desc_build(_shapes(shapes), P, int(R), ctypes.byref(o), arr(grad_ptrs, R * P),
+                           arr(out_ptrs, R), vp(int(gathered_ptr)) if gathered_ptr else None,
+                           arr(full_ptrs, P), blob.ctypes.data, blob.nbytes, ctypes.byref(info))
+    check(st, "tide_desc_build")
+    return blob, info
+
+
+def tide_rs_bf16_to_fp32(h_plan: np.ndarray, d_plan: torch.Tensor, order: int = 0,
+                         max_workgroups: int = 0, stream=None) -> None:
+    check(_lib.lib().tide_rs_bf16_to_fp32(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
+                                          int(max_workgroups), _stream(stream)),
+          "tide_rs_bf16_to_fp32")
+
+
+def tide_ag_place(h_plan: np.ndarray, d_plan: torch.Tensor, max_workgroups: int = 0,
+                  stream=None) -> None:
+    check(_lib.lib().tide_ag_place(h_plan.ctypes.data, d_plan.data_ptr(), int(max_workgroups),
+                                   _stream(stream)), "tide_ag_place")
+
+
+def tide_ag_place_sdma(h_plan: np.ndarray, engine_only: bool = True, stream=None) -> None:
+    check(_lib.lib().tide_ag_place_sdma(h_plan.ctypes.data, 1 if engine_only else 0,
+                                        _stream(stream)), "tide_ag_place_sdma")
+
+
+def _require(t: torch.Tensor, dtype, what: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % what)
+    if t.dtype != dtype:
+        raise TideError(-6, "%s has dtype %s, expected %s" % (what, t.dtype, dtype))
+    if t.device.type != "cuda":
+        raise TideError(-6, "%s is on %s, expected a GPU tensor" % (what, t.device))
+    if not t.is_contiguous():
+        raise TideError(-6, "%s is not contiguous" % what)
+
+
+class Plan:
+    """One layer's descriptor table.
+
+    grads:    R lists of P bf16 tensors (rank q's per-parameter gradients);
+    out:      R fp32 tensors of >= S elements (each rank's shard arena);
+    gathered: one bf16 tensor of >= R*S elements (rank-major slots);
+    full:     P bf16 tensors (the per-parameter full tensors).
+    Either pair may be omitted.  Shapes come from ``shapes`` (torch-style).
+    """
+
+    def __init__(self, shapes, R: int, grads=None, out=None, gathered=None, full=None,
+                 align: int = 1, rs_tile: int = 0, ag_tile: int = 0, flags: int = -1):
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.R = int(R)
+        self.P = len(self.shapes)
+        _, self.m, self.off, self.S = tide_desc_geometry(self.shapes, self.R, align)
+        numels = [int(np.prod(s)) if len(s) else 1 for s in self.shapes]
+        device = None
+        grad_ptrs = out_ptrs = full_ptrs = None
+        gptr = None
+        if grads is not None:
+            if out is None or len(grads) != self.R or len(out) != self.R:
+                raise TideError(-1, "need R gradient lists and R output arenas")
+            grad_ptrs = []
+            for q, gl in enumerate(grads):
+                if len(gl) != self.P:
+                    raise TideError(-1, "rank %d has %d gradients, expected %d" % (q, len(gl), self.P))
+                for p, g in enumerate(gl):
+                    _require(g, torch.bfloat16, "grads[%d][%d]" % (q, p))
+                    if g.numel() != numels[p]:
+                        raise TideError(-1, "grads[%d][%d] has %d elements, expected %d"
+                                        % (q, p, g.numel(), numels[p]))
+                    grad_ptrs.append(g.data_ptr() if g.numel() else 0)
+                    device = g.device
+            out_ptrs = []
+            for r, o in enumerate(out):
+                _require(o, torch.float32, "out[%d]" % r)
+                if o.numel() < self.S:
+                    raise TideError(-1, "out[%d] holds %d floats, need S=%d" % (r, o.numel(), self.S))
+                out_ptrs.append(o.data_ptr())
+                device = o.device
+        if gathered is not None:
+            if full is None or len(full) != self.P:
+                raise TideError(-1, "need P full tensors with the gathered buffer")
+            _require(gathered, torch.bfloat16, "gathered")
+            if gathered.numel() < self.R * self.S:
+                raise TideError(-1, "gathered holds %d elements, need R*S=%d"
+                                % (gathered.numel(), self.R * self.S))
+            gptr = gathered.data_ptr()
+            full_ptrs = []
+            for p, f in enumerate(full):
+                _require(f, torch.bfloat16, "full[%d]" % p)
+                if f.numel() != numels[p]:
+                    raise TideError(-1, "full[%d] has %d elements, expected %d" % (p, f.numel(), numels[p]))
+                full_ptrs.append(f.data_ptr() if f.numel() else 0)
+            device = gathered.device
+        if device is None:
+            raise TideError(-1, "a plan needs gradients or a gathered buffer")
+        self.blob, self.info = tide_desc_build(self.shapes, self.R, grad_ptrs, out_ptrs, gptr,
+                                               full_ptrs, align, rs_tile, ag_tile, flags)
+        used = int(self.info.blob_bytes)
+        self.blob = self.blob[:used].copy()
+        self.d_blob = torch.from_numpy(self.blob).to(device)
+        self._keep = (grads, out, gathered, full)
+
+    def rs(self, order: str = "fixed", max_workgroups: int = 0, stream=None) -> None:
+        tide_rs_bf16_to_fp32(self.blob, self.d_blob, ORDERS[order], max_workgroups, stream)
+
+    def ag(self, max_workgroups: int = 0, stream=None) -> None:
+        tide_ag_place(self.blob, self.d_blob, max_workgroups, stream)
+
+    def ag_sdma(self, engine_only: bool = True, stream=None) -> None:
+        tide_ag_place_sdma(self.blob, engine_only, stream)
+
+    def shard(self, out_arena: torch.Tensor, p: int) -> torch.Tensor:
+        """View of param p's shard in one rank's fp32 arena, shaped [s, rest...]."""
+        shp = self.shapes[p]
+        s = int(self.m[p]) // (int(np.prod(shp[1:])) if len(shp) > 1 else 1) if int(self.m[p]) else 0
+        v = out_arena[int(self.off[p]):int(self.off[p]) + int(self.m[p])]
+        return v.view((s,) + tuple(shp[1:])) if len(shp) else v

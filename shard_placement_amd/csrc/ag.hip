@@ -1,0 +1,175 @@
+// ag.hip -- all-gather placement for gfx950: rank-major bf16 gathered
+// buffer -> per-parameter full tensors, padding rows trimmed.
+//
+// TIDE-AG "delivers shards directly to parameter storage" (Abstract of "The
+// Endgame of FSDP Communication", weekinpapers.com); the gathered buffer is
+// rank-major: each rank's block contiguous, blocks in rank order (kongchang.com
+// article, section "The Root of FSDP2 Communication Overhead").  On one GPU
+// the delivery is the placement step itself: for param p and rank r the
+// clamp(d0 - r*s, 0, s) valid rows of slot r land in rows [r*s, ...) of the
+// full tensor; slot padding is never read.
+//
+// Two engines do it:
+//   tide_ag_place       a compute kernel: one short-lived workgroup per tile
+//                       of up to ag_tile elements; 16-byte loads and stores
+//                       where both ends allow it (4 vectors in flight per
+//                       lane), 4-byte or 2-byte moves otherwise.
+//   tide_ag_place_sdma  host-issued copies on the DMA engines, no compute
+//                       units ("no SMs used for transport or placement",
+//                       same Abstract): one 2-D copy over the ranks whose
+//                       shard is full, one 1-D copy for the partial rank.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstring>
+
+#include "plan_format.h"
+#include "tide.h"
+
+using namespace tide;
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+        return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else
+        *reinterpret_cast<u32x4*>(p) = v;
+}
+
+constexpr int kUnroll = 4;  // 16-byte vectors in flight per lane
+
+template <bool NTL, bool NTS>
+__device__ __forceinline__ void copy_vec16(const uint16_t* __restrict__ src,
+                                           uint16_t* __restrict__ dst, int len) {
+    constexpr int kStep = kBlock * kVec;  // elements per wave-group pass
+    for (int base = 0; base < len; base += kStep * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int e = base + u * kStep + threadIdx.x * kVec;
+            if (e < len) v[u] = ld16<NTL>(src + e);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int e = base + u * kStep + threadIdx.x * kVec;
+            if (e < len) st16<NTS>(dst + e, v[u]);
+        }
+    }
+}
+
+__device__ __forceinline__ void copy_vec4(const uint16_t* __restrict__ src,
+                                          uint16_t* __restrict__ dst, int len) {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+    for (int e = threadIdx.x; e < len / 2; e += kBlock) d[e] = s[e];
+}
+
+__device__ __forceinline__ void copy_scalar(const uint16_t* __restrict__ src,
+                                            uint16_t* __restrict__ dst, int len) {
+    for (int e = threadIdx.x; e < len; e += kBlock) dst[e] = src[e];
+}
+
+template <bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void ag_kernel(const AgTile* __restrict__ tiles,
+                                                    int64_t ntiles,
+                                                    const uint16_t* __restrict__ gathered,
+                                                    const uint64_t* __restrict__ full) {
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const AgTile tile = tiles[t];
+        const uint16_t* src = gathered + tile.src;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(full[tile.p]) + tile.dst;
+        if (tile.kind == kAgVec16)
+            copy_vec16<NTL, NTS>(src, dst, tile.len);
+        else if (tile.kind == kAgVec4)
+            copy_vec4(src, dst, tile.len);
+        else
+            copy_scalar(src, dst, tile.len);
+    }
+}
+
+typedef void (*AgKernel)(const AgTile*, int64_t, const uint16_t*, const uint64_t*);
+
+AgKernel pick(uint32_t flags) {
+    const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
+    if (ntl && nts) return ag_kernel<true, true>;
+    if (ntl) return ag_kernel<true, false>;
+    if (nts) return ag_kernel<false, true>;
+    return ag_kernel<false, false>;
+}
+
+}  // namespace
+
+extern "C" tide_status tide_ag_place(const void* h_plan, const void* d_plan,
+                                     int32_t max_workgroups, tide_stream_t stream) {
+    if (!h_plan || !d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (max_workgroups < 0) return TIDE_EINVAL;
+    if (!h.has_ag) return TIDE_EUNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(d_plan) % 16) return TIDE_EALIGN;
+    if (h.n_ag_tiles == 0) return TIDE_OK;
+
+    const uint8_t* d = static_cast<const uint8_t*>(d_plan);
+    const AgTile* tiles = reinterpret_cast<const AgTile*>(d + h.off_ag);
+    const uint64_t* full = reinterpret_cast<const uint64_t*>(d + h.off_full);
+    const uint16_t* gathered = reinterpret_cast<const uint16_t*>(h.gathered);
+    int64_t ntiles = h.n_ag_tiles;
+
+    int64_t grid = ntiles;
+    if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+    if (grid > INT_MAX) grid = INT_MAX;
+
+    AgKernel k = pick(h.flags);
+    void* args[] = {&tiles, &ntiles, &gathered, &full};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+                                   dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TIDE_OK : TIDE_EHIP;
+}
+
+extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_only,
+                                          tide_stream_t stream) {
+    if (!h_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (engine_only != 0 && engine_only != 1) return TIDE_EINVAL;
+    if (!h.has_ag) return TIDE_EUNSUPPORTED;
+    const uint8_t* b = static_cast<const uint8_t*>(h_plan);
+    const ParamDesc* ps = reinterpret_cast<const ParamDesc*>(b + h.off_params);
+    const uint64_t* full = reinterpret_cast<const uint64_t*>(b + h.off_full);
+    const hipMemcpyKind kind = engine_only ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const char* g = reinterpret_cast<const char*>(h.gathered);
+    for (int32_t p = 0; p < h.P; ++p) {
+        ParamDesc d;
+        std::memcpy(&d, ps + p, sizeof d);
+        if (d.n == 0) continue;
+        char* dst = reinterpret_cast<char*>(full[p]);
+        const int64_t nfull = d.d0 / d.s;  // ranks whose shard has s valid rows
+        if (nfull > 0) {
+            hipError_t e = hipMemcpy2DAsync(dst, (size_t)(2 * d.m), g + 2 * d.off, (size_t)(2 * h.S),
+                                            (size_t)(2 * d.m), (size_t)nfull, kind, s);
+            if (e != hipSuccess) return TIDE_EHIP;
+        }
+        const int64_t rest = d.n - nfull * d.m;  // rows of the one partial rank
+        if (rest > 0 && nfull < h.R) {
+            hipError_t e = hipMemcpyAsync(dst + 2 * nfull * d.m, g + 2 * (nfull * h.S + d.off),
+                                          (size_t)(2 * rest), kind, s);
+            if (e != hipSuccess) return TIDE_EHIP;
+        }
+    }
+    return TIDE_OK;
+}

@@ -1,0 +1,466 @@
+// plan.cpp -- host side of libtide: plan (descriptor table) builder,
+// validation and status strings.  Pure host C++; no HIP call is made here.
+//
+// The plan folds the FSDP2 layout into the kernels' addressing (Abstract of
+// "The Endgame of FSDP Communication", weekinpapers.com: "folding layout
+// placement into collective addressing"): per parameter it records the
+// shard geometry, per (rank, parameter) the gradient pointer, and it cuts
+// every rank's shard into tiles that a workgroup can process without any
+// further layout arithmetic.  Shard geometry follows the library contract
+// in tide.h (rows split in R chunks of ceil(d0/R), +0.0 padding rows,
+// arena offsets rounded up to align_elems).
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "plan_format.h"
+#include "tide.h"
+
+using namespace tide;
+
+namespace {
+
+constexpr int64_t kSection = 256;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// Default reduce-scatter tile: about 256 KB of HBM traffic per tile
+// (R*2 + 4 bytes per element), a power of two in [2048, 32768] elements.
+int32_t default_rs_tile(int32_t R) {
+    int64_t want = (int64_t)262144 / (2 * (int64_t)R + 4);
+    int64_t t = kTileQuantum;
+    while (t * 2 <= want && t < 32768) t *= 2;
+    return (int32_t)t;
+}
+
+constexpr int32_t kDefaultAgTile = 16384;
+constexpr int32_t kDefaultFlags = 0;
+
+struct Resolved {
+    int64_t align;
+    int32_t rs_tile, ag_tile;
+    uint32_t flags;
+};
+
+tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
+    out->align = 1;
+    out->rs_tile = default_rs_tile(R);
+    out->ag_tile = kDefaultAgTile;
+    out->flags = kDefaultFlags;
+    if (!o) return TIDE_OK;
+    if (o->reserved != 0) return TIDE_EINVAL;
+    if (o->align_elems < 1 || o->align_elems > (int64_t)1 << 20) return TIDE_EINVAL;
+    out->align = o->align_elems;
+    if (o->rs_tile_elems != 0) {
+        if (o->rs_tile_elems < 0 || o->rs_tile_elems % kTileQuantum || o->rs_tile_elems > (1 << 24))
+            return TIDE_EINVAL;
+        out->rs_tile = o->rs_tile_elems;
+    }
+    if (o->ag_tile_elems != 0) {
+        if (o->ag_tile_elems < 0 || o->ag_tile_elems % kTileQuantum || o->ag_tile_elems > (1 << 24))
+            return TIDE_EINVAL;
+        out->ag_tile = o->ag_tile_elems;
+    }
+    if (o->flags != -1) {
+        if (o->flags & ~(TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES)) return TIDE_EINVAL;
+        out->flags = (uint32_t)o->flags;
+    }
+    return TIDE_OK;
+}
+
+tide_status geometry(const tide_shape* shapes, int32_t P, int32_t R, int64_t align,
+                     std::vector<ParamDesc>* params, int64_t* S, int64_t* N, int64_t* Npad) {
+    if (P < 0 || R < 1 || R > kMaxRanks) return TIDE_EINVAL;
+    if (P > 0 && !shapes) return TIDE_EINVAL;
+    params->resize(P);
+    int64_t off = 0, n_tot = 0, pad_tot = 0;
+    const int64_t kLimit = (int64_t)1 << 46;  // keeps every product below 2^63
+    for (int32_t p = 0; p < P; ++p) {
+        int64_t d0 = shapes[p].dim0, c = shapes[p].row_numel;
+        if (d0 < 0 || c < 0 || d0 > kLimit || c > kLimit) return TIDE_EINVAL;
+        if (d0 > 0 && c > kLimit / d0) return TIDE_EINVAL;
+        ParamDesc& d = (*params)[p];
+        d.d0 = d0;
+        d.c = c;
+        d.s = ceil_div(d0, R);
+        d.m = d.s * c;
+        d.n = d0 * c;
+        d.off = off;
+        off += round_up(d.m, align);
+        n_tot += d.n;
+        pad_tot += (int64_t)R * d.m;
+        if (off > kLimit || pad_tot > kLimit * 16) return TIDE_EINVAL;
+    }
+    *S = off;
+    *N = n_tot;
+    *Npad = pad_tot;
+    return TIDE_OK;
+}
+
+// Upper bounds of the tile counts, valid for any pointer alignment: a run
+// of L elements becomes at most ceil(L/T) + 2 tiles (scalar head, vector
+// body, scalar tail); each (rank, param) has one valid run and one padding
+// run.
+int64_t rs_tiles_bound(const std::vector<ParamDesc>& ps, int32_t R, int32_t T) {
+    int64_t t = 0;
+    for (const ParamDesc& d : ps)
+        if (d.m > 0) t += (int64_t)R * (2 * ceil_div(d.m, T) + 3);
+    return t;
+}
+
+int64_t ag_tiles_bound(const std::vector<ParamDesc>& ps, int32_t R, int32_t T) {
+    int64_t t = 0;
+    for (const ParamDesc& d : ps)
+        if (d.m > 0) t += (int64_t)R * (ceil_div(d.m, T) + 2);
+    return t;
+}
+
+struct Layout {
+    uint64_t off_params, off_gptr, off_obase, off_full, off_rs, off_ag, bytes;
+};
+
+Layout section_layout(int32_t P, int32_t R, int64_t n_rs, int64_t n_ag) {
+    Layout L;
+    uint64_t pos = kSection;  // header
+    L.off_params = pos;
+    pos += round_up((int64_t)sizeof(ParamDesc) * P, kSection);
+    L.off_gptr = pos;
+    pos += round_up((int64_t)8 * P * R, kSection);
+    L.off_obase = pos;
+    pos += round_up((int64_t)8 * R, kSection);
+    L.off_full = pos;
+    pos += round_up((int64_t)8 * P, kSection);
+    L.off_rs = pos;
+    pos += round_up((int64_t)sizeof(RsTile) * n_rs, kSection);
+    L.off_ag = pos;
+    pos += round_up((int64_t)sizeof(AgTile) * n_ag, kSection);
+    L.bytes = pos;
+    return L;
+}
+
+// Overlap check over address ranges of four classes.
+enum RangeClass { kRsIn = 0, kRsOut = 1, kAgIn = 2, kAgOut = 3 };
+struct Range {
+    uint64_t lo, hi;
+    int cls;
+};
+
+bool ranges_conflict(std::vector<Range>& rs) {
+    std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    uint64_t max_end[4] = {0, 0, 0, 0};
+    bool seen[4] = {false, false, false, false};
+    for (const Range& x : rs) {
+        auto hits = [&](int c) { return seen[c] && max_end[c] > x.lo; };
+        bool bad = false;
+        switch (x.cls) {
+            case kRsOut: bad = hits(kRsIn) || hits(kRsOut); break;
+            case kRsIn: bad = hits(kRsOut); break;
+            case kAgOut: bad = hits(kAgIn) || hits(kAgOut); break;
+            case kAgIn: bad = hits(kAgOut); break;
+        }
+        if (bad) return true;
+        if (!seen[x.cls] || x.hi > max_end[x.cls]) max_end[x.cls] = x.hi;
+        seen[x.cls] = true;
+    }
+    return false;
+}
+
+// Cut the run [jb, je) of param p, rank r into reduce-scatter tiles.
+void cut_rs_run(std::vector<RsTile>& out, int32_t p, int32_t r, int64_t jb, int64_t je,
+                int64_t o_of_jb, bool vec_ok, int64_t phase_elems, int32_t T) {
+    auto emit = [&](int64_t a, int64_t b, int32_t kind) {
+        for (int64_t x = a; x < b; x += T) {
+            RsTile t;
+            t.j0 = x;
+            t.o0 = o_of_jb + (x - jb);
+            t.p = p;
+            t.r = r;
+            t.len = (int32_t)std::min<int64_t>(T, b - x);
+            t.kind = kind;
+            out.push_back(t);
+        }
+    };
+    if (jb >= je) return;
+    if (!vec_ok) {
+        emit(jb, je, kRsScalar);
+        return;
+    }
+    // first j >= jb whose source address is 16-byte aligned in every rank
+    int64_t jv = jb + (((phase_elems - jb) % kVec) + kVec) % kVec;
+    int64_t jend = jv + ((je - jv) / kVec) * kVec;
+    if (jv >= je || jend <= jv) {
+        emit(jb, je, kRsScalar);
+        return;
+    }
+    emit(jb, jv, kRsScalar);
+    emit(jv, jend, kRsVec);
+    emit(jend, je, kRsScalar);
+}
+
+void cut_ag_run(std::vector<AgTile>& out, int32_t p, int64_t src, int64_t dst, int64_t len,
+                uint64_t gaddr, uint64_t faddr, int32_t T) {
+    auto emit = [&](int64_t s0, int64_t d0, int64_t l, int32_t kind) {
+        for (int64_t x = 0; x < l; x += T) {
+            AgTile t;
+            t.src = s0 + x;
+            t.dst = d0 + x;
+            t.p = p;
+            t.len = (int32_t)std::min<int64_t>(T, l - x);
+            t.kind = kind;
+            t.reserved = 0;
+            out.push_back(t);
+        }
+    };
+    if (len <= 0) return;
+    uint64_t sa = gaddr + 2 * (uint64_t)src, da = faddr + 2 * (uint64_t)dst;
+    int32_t kinds[2] = {kAgVec16, kAgVec4};
+    uint64_t widths[2] = {16, 4};
+    for (int k = 0; k < 2; ++k) {
+        uint64_t W = widths[k];
+        if (sa % W != da % W) continue;
+        int64_t head = (int64_t)(((W - sa % W) % W) / 2);
+        int64_t per = (int64_t)W / 2;
+        if (head >= len) break;
+        int64_t body = ((len - head) / per) * per;
+        if (body == 0) break;
+        emit(src, dst, head, kAgScalar);
+        emit(src + head, dst + head, body, kinds[k]);
+        emit(src + head + body, dst + head + body, len - head - body, kAgScalar);
+        return;
+    }
+    emit(src, dst, len, kAgScalar);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tide_abi_version(void) { return TIDE_ABI_VERSION; }
+
+const char* tide_status_str(int32_t status) {
+    switch (status) {
+        case TIDE_OK: return "ok";
+        case TIDE_EINVAL: return "invalid argument";
+        case TIDE_EALIGN: return "pointer not aligned to its element size";
+        case TIDE_EOVERLAP: return "an output range overlaps an input or another output";
+        case TIDE_ENOSPACE: return "plan blob too small";
+        case TIDE_EHIP: return "HIP runtime error";
+        case TIDE_EUNSUPPORTED: return "request not supported by this plan";
+        case TIDE_EPLAN: return "not a tide plan or wrong version";
+        default: return "unknown status";
+    }
+}
+
+tide_status tide_desc_size(const tide_shape* shapes, int32_t P, int32_t R, const tide_opts* opts,
+                           size_t* blob_bytes) {
+    if (!blob_bytes) return TIDE_EINVAL;
+    Resolved o;
+    tide_status st = resolve_opts(opts, R, &o);
+    if (st != TIDE_OK) return st;
+    std::vector<ParamDesc> ps;
+    int64_t S, N, Npad;
+    st = geometry(shapes, P, R, o.align, &ps, &S, &N, &Npad);
+    if (st != TIDE_OK) return st;
+    Layout L = section_layout(P, R, rs_tiles_bound(ps, R, o.rs_tile), ag_tiles_bound(ps, R, o.ag_tile));
+    *blob_bytes = (size_t)L.bytes;
+    return TIDE_OK;
+}
+
+tide_status tide_desc_geometry(const tide_shape* shapes, int32_t P, int32_t R, const tide_opts* opts,
+                               int64_t* chunk_rows, int64_t* shard_numel, int64_t* offsets,
+                               int64_t* slot_numel) {
+    if (!slot_numel) return TIDE_EINVAL;
+    Resolved o;
+    tide_status st = resolve_opts(opts, R, &o);
+    if (st != TIDE_OK) return st;
+    std::vector<ParamDesc> ps;
+    int64_t S, N, Npad;
+    st = geometry(shapes, P, R, o.align, &ps, &S, &N, &Npad);
+    if (st != TIDE_OK) return st;
+    for (int32_t p = 0; p < P; ++p) {
+        if (chunk_rows) chunk_rows[p] = ps[p].s;
+        if (shard_numel) shard_numel[p] = ps[p].m;
+        if (offsets) offsets[p] = ps[p].off;
+    }
+    *slot_numel = S;
+    return TIDE_OK;
+}
+
+tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, const tide_opts* opts,
+                            const void* const* grads, void* const* out_base, const void* gathered,
+                            void* const* full, void* blob, size_t blob_bytes, tide_plan_info* info) {
+    Resolved o;
+    tide_status st = resolve_opts(opts, R, &o);
+    if (st != TIDE_OK) return st;
+    std::vector<ParamDesc> ps;
+    int64_t S, N, Npad;
+    st = geometry(shapes, P, R, o.align, &ps, &S, &N, &Npad);
+    if (st != TIDE_OK) return st;
+    const bool has_rs = grads != nullptr;
+    const bool has_ag = gathered != nullptr;
+    if (has_rs != (out_base != nullptr)) return TIDE_EINVAL;
+    if (has_ag != (full != nullptr)) return TIDE_EINVAL;
+    if (!blob) return TIDE_EINVAL;
+
+    std::vector<Range> ranges;
+    // ---- pointer validation
+    if (has_rs) {
+        for (int32_t r = 0; r < R; ++r) {
+            uint64_t a = (uint64_t)(uintptr_t)out_base[r];
+            if (S > 0 && a == 0) return TIDE_EINVAL;
+            if (a % 4) return TIDE_EALIGN;
+            for (int32_t p = 0; p < P; ++p)
+                if (ps[p].m > 0)
+                    ranges.push_back({a + 4 * (uint64_t)ps[p].off, a + 4 * (uint64_t)(ps[p].off + ps[p].m), kRsOut});
+        }
+        for (int32_t q = 0; q < R; ++q)
+            for (int32_t p = 0; p < P; ++p) {
+                uint64_t a = (uint64_t)(uintptr_t)grads[(int64_t)q * P + p];
+                if (ps[p].n == 0) continue;
+                if (a == 0) return TIDE_EINVAL;
+                if (a % 2) return TIDE_EALIGN;
+                ranges.push_back({a, a + 2 * (uint64_t)ps[p].n, kRsIn});
+            }
+    }
+    if (has_ag) {
+        uint64_t g = (uint64_t)(uintptr_t)gathered;
+        if (g % 2) return TIDE_EALIGN;
+        if (S > 0) ranges.push_back({g, g + 2 * (uint64_t)R * (uint64_t)S, kAgIn});
+        for (int32_t p = 0; p < P; ++p) {
+            uint64_t a = (uint64_t)(uintptr_t)full[p];
+            if (ps[p].n == 0) continue;
+            if (a == 0) return TIDE_EINVAL;
+            if (a % 2) return TIDE_EALIGN;
+            ranges.push_back({a, a + 2 * (uint64_t)ps[p].n, kAgOut});
+        }
+    }
+    if (ranges_conflict(ranges)) return TIDE_EOVERLAP;
+
+    // ---- tiles
+    std::vector<RsTile> rs;
+    std::vector<AgTile> ag;
+    if (has_rs) {
+        rs.reserve((size_t)std::min<int64_t>(rs_tiles_bound(ps, R, o.rs_tile), (int64_t)1 << 24));
+        for (int32_t p = 0; p < P; ++p) {
+            const ParamDesc& d = ps[p];
+            if (d.m == 0) continue;
+            // every rank's source must share one 16-byte phase for the vector path
+            bool vec_ok = true;
+            uint64_t a0 = (uint64_t)(uintptr_t)grads[p];
+            for (int32_t q = 1; q < R && vec_ok; ++q)
+                if (((uint64_t)(uintptr_t)grads[(int64_t)q * P + p]) % 16 != a0 % 16) vec_ok = false;
+            if (d.n == 0) vec_ok = false;
+            // j is 16-byte aligned when (a0 + 2j) % 16 == 0
+            int64_t phase = (int64_t)(((16 - a0 % 16) % 16) / 2);
+            for (int32_t r = 0; r < R; ++r) {
+                int64_t jb = (int64_t)r * d.m, je = std::min<int64_t>(d.n, jb + d.m);
+                if (jb < je) cut_rs_run(rs, p, r, jb, je, d.off, vec_ok, phase, o.rs_tile);
+                int64_t pb = std::max<int64_t>(d.n, jb), pe = jb + d.m;
+                for (int64_t x = pb; x < pe; x += o.rs_tile) {
+                    RsTile t;
+                    t.j0 = x;
+                    t.o0 = d.off + (x - jb);
+                    t.p = p;
+                    t.r = r;
+                    t.len = (int32_t)std::min<int64_t>(o.rs_tile, pe - x);
+                    t.kind = kRsPad;
+                    rs.push_back(t);
+                }
+            }
+        }
+    }
+    if (has_ag) {
+        uint64_t g = (uint64_t)(uintptr_t)gathered;
+        for (int32_t p = 0; p < P; ++p) {
+            const ParamDesc& d = ps[p];
+            if (d.n == 0) continue;
+            for (int32_t r = 0; r < R; ++r) {
+                int64_t v = std::min<int64_t>(std::max<int64_t>(d.d0 - (int64_t)r * d.s, 0), d.s);
+                cut_ag_run(ag, p, (int64_t)r * S + d.off, (int64_t)r * d.m, v * d.c, g,
+                           (uint64_t)(uintptr_t)full[p], o.ag_tile);
+            }
+        }
+    }
+
+    Layout L = section_layout(P, R, (int64_t)rs.size(), (int64_t)ag.size());
+    if (info) {
+        std::memset(info, 0, sizeof(*info));
+        info->R = R;
+        info->P = P;
+        info->slot_numel = S;
+        info->numel = N;
+        info->padded_numel = Npad;
+        info->rs_tiles = (int64_t)rs.size();
+        info->ag_tiles = (int64_t)ag.size();
+        info->rs_tile_elems = o.rs_tile;
+        info->ag_tile_elems = o.ag_tile;
+        info->blob_bytes = (int64_t)L.bytes;
+    }
+    if (blob_bytes < L.bytes) return TIDE_ENOSPACE;
+
+    uint8_t* b = static_cast<uint8_t*>(blob);
+    std::memset(b, 0, (size_t)L.bytes);
+    PlanHeader h;
+    std::memset(&h, 0, sizeof h);
+    h.magic = kMagic;
+    h.version = kVersion;
+    h.R = R;
+    h.P = P;
+    h.align = o.align;
+    h.S = S;
+    h.N = N;
+    h.Npad = Npad;
+    h.rs_tile = o.rs_tile;
+    h.ag_tile = o.ag_tile;
+    h.n_rs_tiles = (int64_t)rs.size();
+    h.n_ag_tiles = (int64_t)ag.size();
+    h.off_params = L.off_params;
+    h.off_gptr = L.off_gptr;
+    h.off_obase = L.off_obase;
+    h.off_full = L.off_full;
+    h.off_rs = L.off_rs;
+    h.off_ag = L.off_ag;
+    h.gathered = (uint64_t)(uintptr_t)gathered;
+    h.bytes = L.bytes;
+    h.has_rs = has_rs ? 1 : 0;
+    h.has_ag = has_ag ? 1 : 0;
+    h.flags = o.flags;
+    std::memcpy(b, &h, sizeof h);
+    if (P) std::memcpy(b + L.off_params, ps.data(), sizeof(ParamDesc) * (size_t)P);
+    uint64_t* gp = reinterpret_cast<uint64_t*>(b + L.off_gptr);
+    uint64_t* ob = reinterpret_cast<uint64_t*>(b + L.off_obase);
+    uint64_t* fp = reinterpret_cast<uint64_t*>(b + L.off_full);
+    if (has_rs) {
+        for (int32_t p = 0; p < P; ++p)
+            for (int32_t q = 0; q < R; ++q)
+                gp[(int64_t)p * R + q] = (uint64_t)(uintptr_t)grads[(int64_t)q * P + p];
+        for (int32_t r = 0; r < R; ++r) ob[r] = (uint64_t)(uintptr_t)out_base[r];
+    }
+    if (has_ag)
+        for (int32_t p = 0; p < P; ++p) fp[p] = (uint64_t)(uintptr_t)full[p];
+    if (!rs.empty()) std::memcpy(b + L.off_rs, rs.data(), sizeof(RsTile) * rs.size());
+    if (!ag.empty()) std::memcpy(b + L.off_ag, ag.data(), sizeof(AgTile) * ag.size());
+    return TIDE_OK;
+}
+
+tide_status tide_plan_query(const void* h_plan, tide_plan_info* info) {
+    if (!h_plan || !info) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    std::memset(info, 0, sizeof(*info));
+    info->R = h.R;
+    info->P = h.P;
+    info->slot_numel = h.S;
+    info->numel = h.N;
+    info->padded_numel = h.Npad;
+    info->rs_tiles = h.n_rs_tiles;
+    info->ag_tiles = h.n_ag_tiles;
+    info->rs_tile_elems = h.rs_tile;
+    info->ag_tile_elems = h.ag_tile;
+    info->blob_bytes = (int64_t)h.bytes;
+    return TIDE_OK;
+}
+
+}  // extern "C"

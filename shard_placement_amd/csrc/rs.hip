@@ -1,0 +1,211 @@
+// rs.hip -- fused bf16 -> fp32 dim-0-shard reduce-scatter for gfx950.
+//
+// TIDE-RS "consumes per-parameter bf16 gradients directly and reduces them
+// into fp32 shards" (Abstract of "The Endgame of FSDP Communication",
+// weekinpapers.com); in a reduce-scatter every rank holds a full buffer and
+// ends with the reduction of its own shard (kongchang.com article, section
+// "The Root of FSDP2 Communication Overhead").  Here all R ranks' gradient
+// tensors sit in one GPU's HBM and are read in place: no rank-major pack
+// buffer, no fp32 staging copy.
+//
+// Work decomposition: the host plan cuts every (param, rank) shard into
+// tiles (plan.cpp); one short-lived 256-lane workgroup takes one tile (or
+// strides over tiles when the grid is capped).  In a vector tile each lane
+// owns 8 consecutive elements: it issues one 16-byte load per rank (a batch
+// of ranks in flight at once), widens bf16 -> fp32 exactly (bits << 16),
+// adds in rank order 0..R-1 starting from rank 0's value, and writes
+// 2 x 16 bytes of fp32.  Padding tiles only write +0.0f.  Every access of a
+// wave is one contiguous 1 KB (loads) / 2 KB (stores) run: fully coalesced.
+// There is no LDS and no inter-workgroup communication.  The path is
+// HBM-bound (about 0.25-0.5 flop per byte), so there is no MFMA here.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstring>
+
+#include "plan_format.h"
+#include "tide.h"
+
+using namespace tide;
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+        return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(float* p, f32x4 v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    else
+        *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// bf16 is the upper half of a binary32, so widening is a shift (exact).
+// A 32-bit word holds elements 2k (low half) and 2k+1 (high half).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ void acc_init(float (&a)[8], u32x4 v) {
+    a[0] = bf_lo(v.x); a[1] = bf_hi(v.x);
+    a[2] = bf_lo(v.y); a[3] = bf_hi(v.y);
+    a[4] = bf_lo(v.z); a[5] = bf_hi(v.z);
+    a[6] = bf_lo(v.w); a[7] = bf_hi(v.w);
+}
+
+// One IEEE binary32 add per element (no multiply, so nothing to contract).
+__device__ __forceinline__ void acc_add(float (&a)[8], u32x4 v) {
+    a[0] = a[0] + bf_lo(v.x); a[1] = a[1] + bf_hi(v.x);
+    a[2] = a[2] + bf_lo(v.y); a[3] = a[3] + bf_hi(v.y);
+    a[4] = a[4] + bf_lo(v.z); a[5] = a[5] + bf_hi(v.z);
+    a[6] = a[6] + bf_lo(v.w); a[7] = a[7] + bf_hi(v.w);
+}
+
+__device__ __forceinline__ const uint16_t* src_of(const uint64_t* gp, int q) {
+    return reinterpret_cast<const uint16_t*>(gp[q]);
+}
+
+// Vector tile, fixed rank order.  RB ranks are loaded per batch; EXACT means
+// R is a multiple of RB (no per-rank guard).  gp: the R source pointers of
+// this param (uniform); j0: first flat index; len % 8 == 0.
+template <int RB, bool EXACT, bool NTL, bool NTS>
+__device__ __forceinline__ void rs_vec_fixed(const uint64_t* __restrict__ gp, int R, int64_t j0,
+                                             int len, float* __restrict__ out) {
+    const bool out16 = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    for (int e = threadIdx.x * kVec; e < len; e += kBlock * kVec) {
+        const int64_t j = j0 + e;
+        float a[8];
+        {
+            u32x4 v[RB];
+            const int nb = EXACT ? RB : (R < RB ? R : RB);
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (EXACT || b < nb) v[b] = load16<NTL>(src_of(gp, b) + j);
+            acc_init(a, v[0]);
+#pragma unroll
+            for (int b = 1; b < RB; ++b)
+                if (EXACT || b < nb) acc_add(a, v[b]);
+        }
+        for (int q0 = RB; q0 < R; q0 += RB) {
+            u32x4 v[RB];
+            const int nb = EXACT ? RB : ((R - q0) < RB ? (R - q0) : RB);
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (EXACT || b < nb) v[b] = load16<NTL>(src_of(gp, q0 + b) + j);
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (EXACT || b < nb) acc_add(a, v[b]);
+        }
+        if (out16) {
+            store16<NTS>(out + e, f32x4{a[0], a[1], a[2], a[3]});
+            store16<NTS>(out + e + 4, f32x4{a[4], a[5], a[6], a[7]});
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) out[e + k] = a[k];
+        }
+    }
+}
+
+// Element-wise tile (unaligned heads and tails, or sources whose 16-byte
+// phases differ between ranks): one element per lane, same order.
+__device__ __forceinline__ void rs_scalar_fixed(const uint64_t* __restrict__ gp, int R, int64_t j0,
+                                                int len, float* __restrict__ out) {
+    for (int e = threadIdx.x; e < len; e += kBlock) {
+        const int64_t j = j0 + e;
+        float a = bf_one(src_of(gp, 0)[j]);
+        for (int q = 1; q < R; ++q) a = a + bf_one(src_of(gp, q)[j]);
+        out[e] = a;
+    }
+}
+
+// Padding rows: +0.0f (all bits clear); nothing is read.
+__device__ __forceinline__ void rs_pad(int len, float* __restrict__ out) {
+    for (int e = threadIdx.x; e < len; e += kBlock) out[e] = 0.0f;
+}
+
+template <int RB, bool EXACT, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restrict__ tiles,
+                                                          int64_t ntiles,
+                                                          const uint64_t* __restrict__ gptr,
+                                                          const uint64_t* __restrict__ obase,
+                                                          int R) {
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const RsTile tile = tiles[t];
+        float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
+        const uint64_t* gp = gptr + (int64_t)tile.p * R;
+        if (tile.kind == kRsVec)
+            rs_vec_fixed<RB, EXACT, NTL, NTS>(gp, R, tile.j0, tile.len, out);
+        else if (tile.kind == kRsScalar)
+            rs_scalar_fixed(gp, R, tile.j0, tile.len, out);
+        else
+            rs_pad(tile.len, out);
+    }
+}
+
+typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int);
+
+template <int RB, bool EXACT>
+RsKernel pick_nt(uint32_t flags) {
+    const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
+    if (ntl && nts) return rs_fixed_kernel<RB, EXACT, true, true>;
+    if (ntl) return rs_fixed_kernel<RB, EXACT, true, false>;
+    if (nts) return rs_fixed_kernel<RB, EXACT, false, true>;
+    return rs_fixed_kernel<RB, EXACT, false, false>;
+}
+
+// Rank batching: small power-of-two R loads every rank at once; R a
+// multiple of 16 loads 16 per batch (64 VGPRs of loads in flight per lane);
+// anything else batches 8 with a guard.
+RsKernel pick_fixed(int R, uint32_t flags) {
+    switch (R) {
+        case 1: return pick_nt<1, true>(flags);
+        case 2: return pick_nt<2, true>(flags);
+        case 4: return pick_nt<4, true>(flags);
+        case 8: return pick_nt<8, true>(flags);
+        default: break;
+    }
+    if (R % 16 == 0) return pick_nt<16, true>(flags);
+    return pick_nt<8, false>(flags);
+}
+
+}  // namespace
+
+extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_plan, int32_t order,
+                                            int32_t max_workgroups, tide_stream_t stream) {
+    if (!h_plan || !d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (order != 0 && order != 1) return TIDE_EINVAL;
+    if (max_workgroups < 0) return TIDE_EINVAL;
+    if (!h.has_rs) return TIDE_EUNSUPPORTED;
+    if (order != 0) return TIDE_EUNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(d_plan) % 16) return TIDE_EALIGN;
+    if (h.n_rs_tiles == 0) return TIDE_OK;
+
+    const uint8_t* d = static_cast<const uint8_t*>(d_plan);
+    const RsTile* tiles = reinterpret_cast<const RsTile*>(d + h.off_rs);
+    const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
+    const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
+    int64_t ntiles = h.n_rs_tiles;
+    int R = h.R;
+
+    int64_t grid = ntiles;
+    if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+    if (grid > INT_MAX) grid = INT_MAX;
+
+    RsKernel k = pick_fixed(R, h.flags);
+    void* args[] = {&tiles, &ntiles, &gptr, &obase, &R};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+                                   dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TIDE_OK : TIDE_EHIP;
+}

@@ -1,0 +1,266 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host logic (geometry, plan builder, validation) is right.
+No compute call is made: plans are built from made-up device addresses and
+the launch entry points are only exercised on arguments they reject before
+touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from shard_placement_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# mirror of the plan blob layout (shard_placement_amd/csrc/plan_format.h)
+HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("R", "<i4"), ("P", "<i4"),
+                ("align", "<i8"), ("S", "<i8"), ("N", "<i8"), ("Npad", "<i8"),
+                ("rs_tile", "<i4"), ("ag_tile", "<i4"), ("n_rs", "<i8"), ("n_ag", "<i8"),
+                ("off_params", "<u8"), ("off_gptr", "<u8"), ("off_obase", "<u8"),
+                ("off_full", "<u8"), ("off_rs", "<u8"), ("off_ag", "<u8"),
+                ("gathered", "<u8"), ("bytes", "<u8"), ("has_rs", "<i4"), ("has_ag", "<i4"),
+                ("flags", "<u4"), ("reserved", "<u4")])
+RS_TILE = np.dtype([("j0", "<i8"), ("o0", "<i8"), ("p", "<i4"), ("r", "<i4"),
+                    ("len", "<i4"), ("kind", "<i4")])
+AG_TILE = np.dtype([("src", "<i8"), ("dst", "<i8"), ("p", "<i4"), ("len", "<i4"),
+                    ("kind", "<i4"), ("reserved", "<i4")])
+PARAM = np.dtype([("d0", "<i8"), ("c", "<i8"), ("s", "<i8"), ("m", "<i8"), ("n", "<i8"),
+                  ("off", "<i8")])
+
+
+def decode(blob):
+    h = np.frombuffer(blob[:HDR.itemsize].tobytes(), HDR)[0]
+
+    def sec(off, n, dt):
+        off, n = int(h[off]), int(n)
+        return np.frombuffer(blob[off:off + np.dtype(dt).itemsize * n].tobytes(), dt)
+
+    rs = sec("off_rs", h["n_rs"], RS_TILE)
+    ag = sec("off_ag", h["n_ag"], AG_TILE)
+    ps = sec("off_params", h["P"], PARAM)
+    gp = sec("off_gptr", int(h["P"]) * int(h["R"]), "<u8")
+    return h, ps, gp, rs, ag
+
+
+def test_library_loads_and_exports_header_symbols():
+    with open(os.path.join(ROOT, "include", "tide.h")) as fh:
+        hdr = fh.read()
+    declared = set(re.findall(r"^\s*(?:tide_status|const char \*|int32_t)\s*\**\s*(tide_\w+)\s*\(",
+                              hdr, re.M))
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    L = _lib.lib()
+    for name in declared:
+        assert hasattr(L, name)
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+    assert L.tide_abi_version() == 1
+    assert L.tide_status_str(-3).decode().startswith("an output range overlaps")
+
+
+SHAPES = [(37, 16), (64, 64), (5,), (), (0, 3), (1001, 8), (6, 5), (3, 0)]
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 17, 64])
+@pytest.mark.parametrize("align", [1, 8])
+def test_geometry_agrees_with_oracle(orc, R, align):
+    s, m, off, S = api.tide_desc_geometry(SHAPES, R, align)
+    os_, om, ooff, oS = orc.layout(SHAPES, R, align)
+    assert list(s) == list(os_) and list(m) == list(om) and list(off) == list(ooff) and S == oS
+
+
+def _fake_ptrs(shapes, R, S, base=1 << 40, grad_misalign=0, out_misalign=0):
+    """Disjoint made-up device addresses: per rank one gradient arena and one
+    output arena, a gathered buffer and full tensors."""
+    numels = [int(np.prod(s)) if len(s) else 1 for s in shapes]
+    pos = base
+    grads, outs, full = [], [], []
+    for q in range(R):
+        p0 = pos + grad_misalign
+        for n in numels:
+            grads.append(p0 if n else 0)
+            p0 += 2 * n
+        pos += ((2 * sum(numels) + grad_misalign + 4095) // 4096 + 1) * 4096
+    for r in range(R):
+        outs.append(pos + out_misalign)
+        pos += ((4 * S + 4095) // 4096 + 1) * 4096
+    gathered = pos
+    pos += ((2 * R * S + 4095) // 4096 + 1) * 4096
+    for n in numels:
+        full.append(pos if n else 0)
+        pos += ((2 * n + 4095) // 4096 + 1) * 4096
+    return grads, outs, gathered, full
+
+
+def _check_rs_tiles(shapes, R, blob, gptrs):
+    h, ps, gp, rs, _ = decode(blob)
+    assert h["magic"] == 0x45444954 and h["has_rs"] == 1
+    covered = {}
+    for t in rs:
+        p, r = int(t["p"]), int(t["r"])
+        d = ps[p]
+        assert r * d["m"] <= t["j0"] and t["j0"] + t["len"] <= (r + 1) * d["m"]
+        assert t["o0"] == d["off"] + t["j0"] - r * d["m"]
+        if t["kind"] == 2:
+            assert t["j0"] >= d["n"]
+        else:
+            assert t["j0"] + t["len"] <= d["n"]
+        if t["kind"] == 0:
+            assert t["len"] % 8 == 0
+            for q in range(R):
+                assert (int(gp[p * R + q]) + 2 * int(t["j0"])) % 16 == 0
+        assert 0 < t["len"] <= h["rs_tile"]
+        covered.setdefault(p, []).append((int(t["j0"]), int(t["j0"] + t["len"])))
+    for p, d in enumerate(ps):
+        runs = sorted(covered.get(p, []))
+        total = R * int(d["m"])
+        pos = 0
+        for a, b in runs:
+            assert a == pos, (p, a, pos)
+            pos = b
+        assert pos == total
+    # pointer table is param-major
+    P = len(shapes)
+    for q in range(R):
+        for p in range(P):
+            assert int(gp[p * R + q]) == int(gptrs[q * P + p])
+
+
+@pytest.mark.parametrize("R", [1, 3, 4, 8, 64])
+@pytest.mark.parametrize("mis", [(0, 0), (2, 4), (6, 8), (14, 12)])
+def test_rs_tiles_partition_every_shard(R, mis):
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S, grad_misalign=mis[0], out_misalign=mis[1])
+    blob, info = api.tide_desc_build(SHAPES, R, g, o, None, None, rs_tile=2048)
+    assert info.rs_tiles > 0 and info.ag_tiles == 0
+    assert info.blob_bytes <= api.tide_desc_size(SHAPES, R, rs_tile=2048)
+    _check_rs_tiles(SHAPES, R, blob, g)
+
+
+def test_rs_vector_tiles_dominate_when_aligned():
+    shapes = [(1024, 8192), (8192,)]
+    R = 8
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    g, o, _, _ = _fake_ptrs(shapes, R, S)
+    blob, info = api.tide_desc_build(shapes, R, g, o)
+    _, _, _, rs, _ = decode(blob)
+    assert set(rs["kind"].tolist()) == {0}
+    assert info.rs_tile_elems == 8192
+    assert int(rs["len"].sum()) == R * S
+
+
+def test_rs_mixed_phases_fall_back_to_scalar():
+    shapes = [(40, 8)]
+    R = 2
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    g, o, _, _ = _fake_ptrs(shapes, R, S)
+    g[1] += 2  # rank 1's gradient two bytes off rank 0's phase
+    blob, _ = api.tide_desc_build(shapes, R, g, o)
+    _, _, _, rs, _ = decode(blob)
+    assert set(rs["kind"].tolist()) == {1}
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 17])
+@pytest.mark.parametrize("gmis", [0, 2, 4, 6])
+def test_ag_tiles_cover_valid_rows_only(R, gmis):
+    _, m, off, S = api.tide_desc_geometry(SHAPES, R)
+    _, _, ga, f = _fake_ptrs(SHAPES, R, S)
+    blob, info = api.tide_desc_build(SHAPES, R, None, None, ga + gmis, f, ag_tile=2048)
+    h, ps, _, _, ag = decode(blob)
+    assert h["has_rs"] == 0 and h["has_ag"] == 1 and info.rs_tiles == 0
+    for p, d in enumerate(ps):
+        tiles = sorted((int(t["dst"]), int(t["src"]), int(t["len"]), int(t["kind"]))
+                       for t in ag if t["p"] == p)
+        pos = 0
+        for dst, src, ln, kind in tiles:
+            assert dst == pos
+            r = dst // int(d["m"])
+            assert src == r * S + int(d["off"]) + (dst - r * int(d["m"]))
+            if kind == 0:
+                assert (ga + gmis + 2 * src) % 16 == 0 and (f[p] + 2 * dst) % 16 == 0 and ln % 8 == 0
+            if kind == 1:
+                assert (ga + gmis + 2 * src) % 4 == 0 and (f[p] + 2 * dst) % 4 == 0 and ln % 2 == 0
+            # never crosses into the rank's padding rows
+            valid = min(max(int(d["d0"]) - r * int(d["s"]), 0), int(d["s"])) * int(d["c"])
+            assert dst + ln <= r * int(d["m"]) + valid
+            pos = dst + ln
+        assert pos == int(d["n"])
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+    except _lib.TideError as e:
+        return e.status
+    return 0
+
+
+def test_validation_errors():
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S)
+    b = api.tide_desc_build
+    assert _status(b, SHAPES, 0, g, o, None, None) == -1          # R < 1
+    assert _status(b, SHAPES, R, g, None, None, None) == -1       # grads without outputs
+    assert _status(b, SHAPES, R, g, o, ga, None) == -1            # gathered without full
+    g2 = list(g); g2[0] = 0
+    assert _status(b, SHAPES, R, g2, o, None, None) == -1         # NULL gradient
+    g2 = list(g); g2[1] += 1
+    assert _status(b, SHAPES, R, g2, o, None, None) == -2         # odd bf16 address
+    o2 = list(o); o2[0] += 2
+    assert _status(b, SHAPES, R, g, o2, None, None) == -2         # misaligned fp32 arena
+    o2 = list(o); o2[1] = o2[0]
+    assert _status(b, SHAPES, R, g, o2, None, None) == -3         # two ranks share an arena
+    o2 = list(o); o2[2] = g[5]
+    assert _status(b, SHAPES, R, g, o2, None, None) == -3         # output over a gradient
+    f2 = list(f); f2[0] = ga + 64
+    assert _status(b, SHAPES, R, None, None, ga, f2) == -3        # full over the gathered buffer
+    # Slot-Reuse: outputs inside the gathered buffer are allowed
+    o3 = [ga + 4 * S * r for r in range(R)]
+    assert _status(b, SHAPES, R, g, o3, ga, f) == 0
+    # identical ranks may alias one gradient tensor
+    g4 = g[:len(SHAPES)] * R
+    assert _status(b, SHAPES, R, g4, o, None, None) == 0
+    assert _status(b, [(-1, 2)], R, [1 << 40] * R, o, None, None) == -1
+    assert _status(b, SHAPES, R, g, o, None, None, 1, 1000) == -1  # tile not a multiple of 2048
+
+
+def test_enospace_reports_needed_size():
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, _, _ = _fake_ptrs(SHAPES, R, S)
+    L = _lib.lib()
+    shp = api._shapes(SHAPES)
+    info = _lib.TidePlanInfo()
+    opts = api._opts()
+    vp = ctypes.c_void_p
+    garr = (vp * len(g))(*[x or None for x in g])
+    oarr = (vp * R)(*o)
+    buf = np.zeros(64, np.uint8)
+    st = L.tide_desc_build(shp, len(SHAPES), R, ctypes.byref(opts), garr, oarr, None, None,
+                           buf.ctypes.data, buf.nbytes, ctypes.byref(info))
+    assert st == -4 and info.blob_bytes > 64
+
+
+def test_launches_reject_before_touching_the_gpu():
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S)
+    L = _lib.lib()
+    blob, _ = api.tide_desc_build(SHAPES, R, g, o, None, None)
+    fake_dev = ctypes.c_void_p(1 << 44)
+    assert L.tide_rs_bf16_to_fp32(blob.ctypes.data, fake_dev, 2, 0, None) == -1   # bad order
+    assert L.tide_rs_bf16_to_fp32(blob.ctypes.data, fake_dev, 0, -1, None) == -1  # bad grid cap
+    assert L.tide_rs_bf16_to_fp32(blob.ctypes.data, ctypes.c_void_p((1 << 44) + 8), 0, 0, None) == -2
+    assert L.tide_ag_place(blob.ctypes.data, fake_dev, 0, None) == -6             # no AG pointers
+    assert L.tide_ag_place_sdma(blob.ctypes.data, 1, None) == -6
+    junk = np.zeros(4096, np.uint8)
+    assert L.tide_rs_bf16_to_fp32(junk.ctypes.data, fake_dev, 0, 0, None) == -7
+    assert L.tide_ag_place(junk.ctypes.data, fake_dev, 0, None) == -7
+    info = _lib.TidePlanInfo()
+    assert L.tide_plan_query(junk.ctypes.data, ctypes.byref(info)) == -7
+    assert L.tide_plan_query(blob.ctypes.data, ctypes.byref(info)) == 0
+    assert info.R == R and info.slot_numel == S
+    ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
+    assert L.tide_rs_bf16_to_fp32(ag_blob.ctypes.data, fake_dev, 0, 0, None) == -6

@@ -1,0 +1,163 @@
+"""GPU parity of the all-gather placement (tide_ag_place on the compute
+units, tide_ag_place_sdma on the copy engines) against the CPU oracle: bit
+for bit, always (it is a pure move)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from shard_placement_amd import api, configs, harness, synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _wl(shapes, R, key=300, sigma=1.0):
+    shapes = tuple(tuple(s) for s in shapes)
+    return configs.Workload(key=key, name="adhoc", R=R, names=tuple("p%d" % i for i in range(len(shapes))),
+                            shapes=shapes, sigma=sigma)
+
+
+@pytest.mark.parametrize("engine", ["cu", "sdma", "sdma-any"])
+def test_tiny_workload_bitwise(engine):
+    w = configs.get(1)
+    gu.say("tiny ag", engine)
+    st = harness.setup(w, with_rs=False, gen_device="cpu")
+    if engine == "cu":
+        st.plan.ag()
+    else:
+        st.plan.ag_sdma(engine_only=(engine == "sdma"))
+    torch.cuda.synchronize()
+    gu.check_ag_full(st)
+
+
+CASES = [
+    (1, [(37, 16), (5,)]),
+    (3, [(37, 16), (64, 64), (5,), ()]),
+    (4, [(1001, 3), (0, 5), (2, 2, 2), (9,)]),
+    (8, [(8192,), (1024, 64), (6, 40)]),
+    (17, [(300, 16), (1,)]),
+    (32, [(6, 5120), (5120,)]),
+    (64, [(1001, 64), (128,), (3, 8)]),
+]
+
+
+@pytest.mark.parametrize("R,shapes", CASES, ids=[str(c[0]) for c in CASES])
+@pytest.mark.parametrize("engine", ["cu", "sdma"])
+@pytest.mark.parametrize("tile", [0, 2048])
+def test_ragged_shapes_bitwise(R, shapes, engine, tile):
+    if engine == "sdma" and tile:
+        pytest.skip("the copy-engine path has no tiles")
+    w = _wl(shapes, R, key=310 + R)
+    gu.say("ragged ag", R, shapes, engine, tile)
+    st = harness.setup(w, with_rs=False, ag_tile=tile)
+    st.plan.ag() if engine == "cu" else st.plan.ag_sdma()
+    torch.cuda.synchronize()
+    gu.check_ag_full(st)
+
+
+@pytest.mark.parametrize("gshift", [1, 2, 3, 4, 5, 7])
+@pytest.mark.parametrize("engine", ["cu", "sdma"])
+def test_unaligned_gathered_buffer(gshift, engine):
+    """The gathered buffer starts gshift elements into an allocation, so
+    slots and full tensors disagree in 16-byte (or 4-byte) phase."""
+    shapes = [(333, 24), (5,), (64, 7), (2048, 8)]
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    big = torch.empty(R * S + 8, dtype=torch.bfloat16, device="cuda")
+    synth.bits_(big, 400 + gshift)
+    gathered = big[gshift:gshift + R * S]
+    n = synth.arena_numel(shapes)
+    fa = torch.empty(n + 32, dtype=torch.bfloat16, device="cuda")
+    fa.view(torch.int16).fill_(-1)
+    full = synth.views(fa[16:16 + n], shapes)
+    plan = api.Plan(shapes, R, gathered=gathered, full=full)
+    gu.say("unaligned ag", gshift, engine)
+    plan.ag() if engine == "cu" else plan.ag_sdma()
+    torch.cuda.synchronize()
+    want = [np.full(gu.numel(s), gu.SENT16, np.uint16) for s in shapes]
+    oracle.ag(shapes, R, gu.bits16(gathered), out=want)
+    for p in range(len(shapes)):
+        gu.assert_bits_equal(gu.bits16(full[p]), want[p], "full[%d]" % p)
+    f = gu.bits16(fa)
+    assert np.all(f[:16] == gu.SENT16) and np.all(f[16 + n:] == gu.SENT16)
+
+
+def test_placement_of_rs_output_is_full_fold():
+    """AG(bf16(RS shards)) equals bf16 of the full fold, all on the device."""
+    shapes = [(1001, 24), (5,), (64, 64)]
+    R = 8
+    w = _wl(shapes, R, key=330)
+    st = harness.setup(w, with_ag=False)
+    st.plan.rs()
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    gathered = torch.cat([o.to(torch.bfloat16) for o in st.out])
+    n = synth.arena_numel(shapes)
+    fa = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    full = synth.views(fa, shapes)
+    plan = api.Plan(shapes, R, gathered=gathered, full=full)
+    plan.ag()
+    torch.cuda.synchronize()
+    for p, shp in enumerate(shapes):
+        folds = oracle.fold_points(np.stack([gu.bits16(st.grads[q][p]) for q in range(R)], axis=1))
+        want = gu.bits16(torch.from_numpy(folds).to(torch.bfloat16))
+        gu.assert_bits_equal(gu.bits16(full[p]), want, "param %d" % p)
+
+
+def test_random_bit_patterns_round_trip():
+    """Slots cut from random bit patterns (NaN payloads, -0, inf) with
+    torch.chunk come back bit for bit; padding sentinels never appear."""
+    shapes = [(37, 16), (64, 64), (5,), (1001, 3)]
+    R = 4
+    fulls = []
+    for p, s in enumerate(shapes):
+        t = torch.empty(s, dtype=torch.bfloat16)
+        synth.bits_(t, 500 + p)
+        t.view(torch.int16)[t.view(torch.int16) == -1] = 0x7FC1
+        fulls.append(t)
+    slots = []
+    for r in range(R):
+        pieces = []
+        for t in fulls:
+            d0 = t.shape[0]
+            sr = -(-d0 // R)
+            ch = list(torch.chunk(t, R, dim=0))
+            c = ch[r] if r < len(ch) else t[0:0]
+            pad = torch.full((sr - c.shape[0],) + tuple(t.shape[1:]), -1, dtype=torch.int16)
+            pieces.append(torch.cat([c.view(torch.int16), pad]).reshape(-1))
+        slots.append(torch.cat(pieces))
+    gathered = torch.cat(slots).view(torch.bfloat16).to("cuda")
+    n = synth.arena_numel(shapes)
+    fa = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    full = synth.views(fa, shapes)
+    for engine in ("cu", "sdma"):
+        fa.view(torch.int16).fill_(0x1234)
+        plan = api.Plan(shapes, R, gathered=gathered, full=full)
+        plan.ag() if engine == "cu" else plan.ag_sdma()
+        torch.cuda.synchronize()
+        for p, t in enumerate(fulls):
+            assert torch.equal(full[p].cpu().view(torch.int16), t.view(torch.int16)), (engine, p)
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
+def test_full_size_placement(key):
+    w = configs.get(key)
+    gu.say("full-size ag", w.name)
+    st = harness.setup(w, with_rs=False, guard=64)
+    for engine in ("cu", "sdma"):
+        st.full_arena.view(torch.int16).fill_(-1)
+        st.plan.ag() if engine == "cu" else st.plan.ag_sdma()
+        torch.cuda.synchronize()
+        gu.say("oracle ag compare", w.name, engine)
+        gu.check_ag_full(st)
+    st.free()
+    torch.cuda.empty_cache()

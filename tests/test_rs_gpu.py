@@ -1,0 +1,252 @@
+"""GPU parity of the fused reduce-scatter (tide_rs_bf16_to_fp32) against the
+CPU oracle: bit for bit in fixed rank order, on small and ragged problems
+in full and on the full-size workloads on sampled elements, plus properties
+that hold at any size (summation bound for every element, +0.0 padding,
+untouched guard bands, determinism)."""
+import numpy as np
+import pytest
+import torch
+
+from shard_placement_amd import api, configs, harness, synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _wl(shapes, R, key=90, sigma=1.0, name="adhoc"):
+    shapes = tuple(tuple(s) for s in shapes)
+    return configs.Workload(key=key, name=name, R=R, names=tuple("p%d" % i for i in range(len(shapes))),
+                            shapes=shapes, sigma=sigma)
+
+
+def _run(st, order="fixed", max_wg=0):
+    st.plan.rs(order=order, max_workgroups=max_wg)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_tiny_workload_bitwise(flags):
+    w = configs.get(1)
+    gu.say("tiny rs flags", flags)
+    st = harness.setup(w, with_ag=False, gen_device="cpu", flags=flags)
+    _run(st)
+    gu.check_rs_full(st)
+
+
+RANDOM_CASES = [
+    (1, [(37, 16), (5,)]),
+    (2, [(64, 64), (3,), ()]),
+    (3, [(37, 16), (64, 64), (5,)]),
+    (4, [(1001, 3), (0, 5), (2, 2, 2), (9,)]),
+    (5, [(130, 24), (7, 1)]),
+    (7, [(1, 1), (100, 40)]),
+    (8, [(8192,), (1024, 64), (6, 40)]),
+    (9, [(77, 33)]),
+    (16, [(512, 48), (1,), (17, 8)]),
+    (17, [(300, 16)]),
+    (32, [(6, 5120), (5120,)]),
+    (33, [(65, 32)]),
+    (64, [(1001, 64), (128,), (3, 8)]),
+]
+
+
+@pytest.mark.parametrize("R,shapes", RANDOM_CASES, ids=[str(c[0]) for c in RANDOM_CASES])
+@pytest.mark.parametrize("tile", [0, 2048])
+def test_ragged_shapes_bitwise(R, shapes, tile):
+    w = _wl(shapes, R, key=100 + R)
+    gu.say("ragged rs R", R, shapes, "tile", tile)
+    st = harness.setup(w, with_ag=False, rs_tile=tile)
+    _run(st)
+    gu.check_rs_full(st)
+
+
+@pytest.mark.parametrize("align", [4, 8, 64])
+def test_aligned_offsets_leave_gaps(align):
+    w = _wl([(37, 16), (5,), (3, 3), (40, 8)], 4, key=131)
+    gu.say("align", align)
+    st = harness.setup(w, with_ag=False, align=align)
+    _run(st)
+    gu.check_rs_full(st)
+
+
+def _custom(shapes, R, phases, out_shift=0, key=140):
+    """Gradients as views at element offset phases[q] of a larger tensor, so
+    ranks have different 16-byte phases (the element-wise path) or the same
+    odd phase (scalar heads and tails around a vector body)."""
+    w = _wl(shapes, R, key=key)
+    n = synth.arena_numel(shapes)
+    st = harness.Setup(w=w, device=torch.device("cuda"), arenas=[], grads=[], out=[], out_alloc=[])
+    for q in range(R):
+        big = torch.empty(n + 16, dtype=torch.bfloat16, device="cuda")
+        synth.fill_normal_(big, 1000 * key + q, 1.0)
+        a = big[phases[q]:phases[q] + n]
+        st.arenas.append(big)
+        st.grads.append(synth.views(a, shapes))
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    st.S, st.guard = S, 8
+    for r in range(R):
+        buf = torch.empty(S + 16 + out_shift, dtype=torch.float32, device="cuda")
+        buf.view(torch.int32).fill_(-1)
+        st.out_alloc.append(buf)
+        st.out.append(buf[8 + out_shift:8 + out_shift + S])
+    st.plan = api.Plan(shapes, R, grads=st.grads, out=st.out)
+    return st
+
+
+@pytest.mark.parametrize("phases", [[0, 1, 2, 3], [3, 3, 3, 3], [5, 5, 5, 5], [0, 0, 4, 0]])
+@pytest.mark.parametrize("out_shift", [0, 1, 2, 3])
+def test_unaligned_sources_and_outputs(phases, out_shift):
+    shapes = [(333, 24), (5,), (64, 7)]
+    gu.say("unaligned", phases, out_shift)
+    st = _custom(shapes, 4, phases, out_shift)
+    _run(st)
+    w = st.w
+    want = [np.full(st.S, np.nan, np.float32) for _ in range(4)]
+    for a in want:
+        a.view(np.uint32)[:] = gu.NAN32
+    import oracle
+    oracle.rs(w.shapes, 4, gu.grads_np(st), out=want)
+    for r in range(4):
+        gu.assert_bits_equal(gu.bits32(st.out[r]), want[r].view(np.uint32), "rank %d" % r)
+        a = gu.bits32(st.out_alloc[r])
+        assert np.all(a[:8 + out_shift] == gu.NAN32) and np.all(a[8 + out_shift + st.S:] == gu.NAN32)
+
+
+def test_special_values():
+    """±0, subnormals, ±inf, NaN, bf16 max: identical to the oracle (a NaN
+    matches any NaN)."""
+    R = 5
+    shapes = [(64, 40)]
+    w = _wl(shapes, R, key=150)
+    gu.say("special values")
+    st = harness.setup(w, with_ag=False)
+    vals = list(synth.SPECIAL_BF16.values())
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for q in range(R):
+        pick = torch.randint(0, len(vals), (64 * 40,), generator=gen)
+        bits = torch.tensor(vals, dtype=torch.int32)[pick].to(torch.int16)
+        st.arenas[q].view(torch.int16).copy_(bits.to("cuda"))
+    _run(st)
+    gu.check_rs_full(st, nan_as_class=True)
+
+
+@pytest.mark.parametrize("max_wg", [1, 3, 64, 1000])
+def test_capped_grid_same_bits(max_wg):
+    w = _wl([(1001, 24), (5,), (64, 64)], 8, key=160)
+    gu.say("max_wg", max_wg)
+    st = harness.setup(w, with_ag=False, rs_tile=2048)
+    _run(st, max_wg=max_wg)
+    gu.check_rs_full(st)
+
+
+def test_deterministic_repeat():
+    w = _wl([(4096, 256), (7,)], 16, key=170, sigma=1e-3)
+    st = harness.setup(w, with_ag=False)
+    _run(st)
+    first = [o.clone() for o in st.out]
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    _run(st)
+    for a, b in zip(first, st.out):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("R", [2, 3, 8, 17, 64])
+def test_identical_ranks_alias_one_tensor(R):
+    """Every rank passes the same tensor: the result is R*g exactly."""
+    shapes = [(100, 24), (3,)]
+    w = _wl(shapes, R, key=180)
+    n = synth.arena_numel(shapes)
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    synth.fill_normal_(a, 181, 1.0)
+    g = synth.views(a, shapes)
+    _, m, off, S = api.tide_desc_geometry(shapes, R)
+    out = [torch.full((S,), float("nan"), device="cuda") for _ in range(R)]
+    plan = api.Plan(shapes, R, grads=[g] * R, out=out)
+    plan.rs()
+    torch.cuda.synchronize()
+    for p, shp in enumerate(shapes):
+        flat = torch.cat([out[r][int(off[p]):int(off[p]) + int(m[p])] for r in range(R)]).cpu()
+        nn = gu.numel(shp)
+        want = (g[p].reshape(-1).double() * R).float().cpu()
+        assert torch.equal(flat[:nn].view(torch.int32), want.view(torch.int32))
+        assert torch.all(flat[nn:].view(torch.int32) == 0)
+
+
+@pytest.mark.parametrize("R", [2, 4, 8])
+def test_slot_reuse_same_bits_no_allocation(R):
+    w = _wl([(1001, 40), (5,), (64, 64)], R, key=190, sigma=1e-3)
+    gu.say("slot reuse R", R)
+    ref = harness.setup(w, with_ag=False, slot_reuse=False)
+    _run(ref)
+    st = harness.setup(w, with_ag=True, slot_reuse=True)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    st.plan.ag()   # the gathered buffer is used first ...
+    st.plan.rs()   # ... then vacated and reused for the fp32 shards
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    for r in range(R):
+        assert torch.equal(st.out[r].view(torch.int32), ref.out[r].view(torch.int32))
+        gu.check_out_guards(st, r)
+        assert st.out[r].data_ptr() == st.vacated[r].data_ptr()
+
+
+# ------------------------------------------------------------ full size
+def _free_gb():
+    free, _ = torch.cuda.mem_get_info()
+    return free / 1e9
+
+
+def _need_gb(w, slot_reuse):
+    n = w.numel()
+    _, _, _, S = api.tide_desc_geometry(w.shapes, w.R)
+    g = w.R * n * 2
+    outs = w.R * 2 * S * w.R if slot_reuse else w.R * 4 * S
+    return (g + outs + 2 * n + (0 if slot_reuse else 2 * w.R * S)) / 1e9 + 2
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
+def test_full_size_workload(key):
+    w = configs.get(key)
+    need = _need_gb(w, w.slot_reuse)
+    if _free_gb() < need:
+        pytest.skip("needs %.0f GB of free HBM" % need)
+    gu.say("full-size", w.name, "R", w.R, "need GB", round(need))
+    st = harness.setup(w, guard=64)
+    torch.cuda.synchronize()
+    st.plan.ag()
+    st.plan.rs()
+    torch.cuda.synchronize()
+    gu.say("sampled oracle check", w.name)
+    n = gu.check_rs_sampled(st)
+    assert n > 0
+    gu.say("bound check over every element", w.name)
+    gu.check_rs_bound_all(st)
+    for r in range(w.R):
+        gu.check_out_guards(st, r)
+    if key == 2:
+        gu.check_rs_by_param(st, range(w.P))
+    if key == 4:
+        gu.check_rs_by_param(st, [10, 11, 12])          # modulation (26 empty shards), norms
+    if key == 5:
+        gu.check_rs_by_param(st, [w.P - 1, 7])          # the ragged param, a norm
+    # determinism at full size
+    snap = [o.clone() for o in st.out[:2]]
+    st.plan.rs()
+    torch.cuda.synchronize()
+    for a, b in zip(snap, st.out[:2]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    st.free()
+    del snap
+    torch.cuda.empty_cache()
