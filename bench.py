@@ -108,60 +108,6 @@ def cpu_baseline(st, budget_s: float):
     }
 
 
-def gemm_probe(st, iters: int = 50):
-    """Single-wave bf16 GEMM alone and beside the reduce-scatter.  Returns a
-    dict of times and the slowdown; the GEMM runs on a second stream."""
-    import torch
-
-    M, N, K = 4096, 4096, 8192
-    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
-    b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
-    c = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
-    side = torch.cuda.Stream()
-    main = torch.cuda.current_stream()
-
-    def gemm_times(n):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        with torch.cuda.stream(side):
-            for e0, e1 in evs:
-                e0.record()
-                torch.matmul(a, b, out=c)
-                e1.record()
-        return evs
-
-    for _ in range(5):
-        torch.matmul(a, b, out=c)
-    torch.cuda.synchronize()
-    alone = gemm_times(iters)
-    torch.cuda.synchronize()
-    t0 = sorted(e0.elapsed_time(e1) for e0, e1 in alone)[iters // 2]
-    # concurrent: a train of reduce-scatters on the main stream, GEMMs beside it
-    rs0 = torch.cuda.Event(enable_timing=True)
-    rs1 = torch.cuda.Event(enable_timing=True)
-    n_rs = max(1, int(iters * t0 / 3.0) + 2)
-    rs0.record(main)
-    for _ in range(n_rs):
-        st.plan.rs(stream=main)
-    rs1.record(main)
-    side.wait_event(rs0)
-    conc = gemm_times(iters)
-    torch.cuda.synchronize()
-    inside = []
-    rs_start = 0.0
-    rs_end = rs0.elapsed_time(rs1)
-    for e0, e1 in conc:
-        s = rs0.elapsed_time(e0)
-        e = rs0.elapsed_time(e1)
-        if rs_start <= s and e <= rs_end:
-            inside.append(e0.elapsed_time(e1))
-    t1 = sorted(inside)[len(inside) // 2] if inside else None
-    return {"gemm": "bf16 %dx%dx%d torch.matmul" % (M, N, K), "t_alone_ms": round(t0, 4),
-            "t_concurrent_ms": round(t1, 4) if t1 else None, "n_inside": len(inside),
-            "rs_launches": n_rs,
-            "slowdown_pct": round(100.0 * (t1 / t0 - 1.0), 2) if t1 else None}
-
-
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,10 +148,12 @@ def main():
         st.plan.info.ag_tiles, st.plan.info.ag_tile_elems, st.plan.info.blob_bytes))
 
     if args.calib_copy_mib > 0:
+        # a plain elementwise kernel of known traffic (reads and writes
+        # calib_copy_mib MiB each) for scaling the HBM byte counters
         src = torch.empty(args.calib_copy_mib << 19, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
         src.fill_(1.0)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -257,9 +205,13 @@ def main():
                 "engine": "hipMemcpyDeviceToDeviceNoCU copies (2-D per param + 1-D partial rank)"}
         log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
 
-    probe = gemm_probe(st) if args.probe else None
-    if probe:
-        log("probe", probe)
+    probe = None
+    if args.probe:
+        from shard_placement_amd import probe as probe_mod
+
+        probe = probe_mod.run(st.plan, rsb)
+        for m in probe["modes"]:
+            log("probe", m)
 
     traffic = read_traffic("rs", w.name, RS_SOURCES)
     cpu = None
@@ -291,7 +243,7 @@ def main():
         "ag_frac_hbm": round(ag_gbs / HBM_PEAK_GBS, 4),
         "ag_ms": round(ag_avg, 4),
         "ag_sdma": sdma,
-        "gemm_slowdown_pct": probe["slowdown_pct"] if probe else None,
+        "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
         "probe": probe,
         "roofline": {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rs_gbs / HBM_PEAK_GBS, 4),

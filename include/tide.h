@@ -89,9 +89,9 @@ typedef struct tide_shape {
 typedef struct tide_opts {
     int64_t align_elems;   /* arena/slot offset alignment, elements (>= 1; default 1) */
     int32_t rs_tile_elems; /* elements per reduce-scatter tile, multiple of 2048
-                              (0: chosen from R) */
-    int32_t ag_tile_elems; /* elements per placement tile, multiple of 2048 (0: 16384) */
-    int32_t flags;         /* -1: library default; else an OR of TIDE_FLAG_* */
+                              (0: chosen from R, about 128 KB of traffic) */
+    int32_t ag_tile_elems; /* elements per placement tile, multiple of 2048 (0: 2048) */
+    int32_t flags;         /* -1: library default (both hints); else an OR of TIDE_FLAG_* */
     int32_t reserved;      /* must be 0 */
 } tide_opts;
 
@@ -181,6 +181,15 @@ tide_status tide_ag_place(const void *h_plan, const void *d_plan,
  * kind; 0 lets the runtime choose. */
 tide_status tide_ag_place_sdma(const void *h_plan, int32_t engine_only,
                                tide_stream_t stream);
+
+/* A stream whose kernels may run only on the first n_cu compute units of
+ * the device's CU mask (hipExtStreamCreateWithCUMask; default priority), for
+ * confining the reduce-scatter's workgroups to part of the chip next to
+ * concurrent compute [Abstract: interference with a concurrent GEMM].
+ * n_cu in [1, number of CUs]; *out receives the stream; release it with
+ * tide_stream_destroy.  Creating a stream synchronises nothing. */
+tide_status tide_stream_create_cu_limited(int32_t n_cu, tide_stream_t *out);
+tide_status tide_stream_destroy(tide_stream_t stream);
 
 /* Static text for a status code. */
 const char *tide_status_str(int32_t status);

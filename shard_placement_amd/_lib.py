@@ -21,7 +21,7 @@ FLAG_NT_STORES = 2
 # Every symbol include/tide.h declares.
 EXPORTS = ("tide_abi_version", "tide_status_str", "tide_desc_size", "tide_desc_geometry",
            "tide_desc_build", "tide_plan_query", "tide_rs_bf16_to_fp32", "tide_ag_place",
-           "tide_ag_place_sdma")
+           "tide_ag_place_sdma", "tide_stream_create_cu_limited", "tide_stream_destroy")
 
 
 class TideShape(ctypes.Structure):
@@ -88,8 +88,11 @@ def lib():
     L.tide_rs_bf16_to_fp32.argtypes = [vp, vp, i32, i32, vp]
     L.tide_ag_place.argtypes = [vp, vp, i32, vp]
     L.tide_ag_place_sdma.argtypes = [vp, i32, vp]
+    L.tide_stream_create_cu_limited.argtypes = [i32, ctypes.POINTER(vp)]
+    L.tide_stream_destroy.argtypes = [vp]
     for name in ("tide_desc_size", "tide_desc_geometry", "tide_desc_build", "tide_plan_query",
-                 "tide_rs_bf16_to_fp32", "tide_ag_place", "tide_ag_place_sdma"):
+                 "tide_rs_bf16_to_fp32", "tide_ag_place", "tide_ag_place_sdma",
+                 "tide_stream_create_cu_limited", "tide_stream_destroy"):
         getattr(L, name).restype = ctypes.c_int
     if L.tide_abi_version() != 1:
         raise RuntimeError("libtide ABI version %d, expected 1" % L.tide_abi_version())

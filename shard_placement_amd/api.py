@@ -121,6 +121,20 @@ def tide_ag_place_sdma(h_plan: np.ndarray, engine_only: bool = True, stream=None
                                         _stream(stream)), "tide_ag_place_sdma")
 
 
+def tide_stream_create_cu_limited(n_cu: int) -> torch.cuda.ExternalStream:
+    """A torch stream wrapping a HIP stream confined to the first n_cu CUs.
+    Release it with tide_stream_destroy."""
+    h = ctypes.c_void_p(0)
+    check(_lib.lib().tide_stream_create_cu_limited(int(n_cu), ctypes.byref(h)),
+          "tide_stream_create_cu_limited")
+    return torch.cuda.ExternalStream(int(h.value))
+
+
+def tide_stream_destroy(stream) -> None:
+    check(_lib.lib().tide_stream_destroy(ctypes.c_void_p(int(stream.cuda_stream))),
+          "tide_stream_destroy")
+
+
 def _require(t: torch.Tensor, dtype, what: str) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % what)

@@ -32,20 +32,25 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// All buffers are device global memory: global_* instead of flat_* accesses.
+#define TIDE_GLOBAL __attribute__((address_space(1)))
+
 template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+    const TIDE_GLOBAL u32x4* g = (const TIDE_GLOBAL u32x4*)(p);
     if constexpr (NT)
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return __builtin_nontemporal_load(g);
     else
-        return *reinterpret_cast<const u32x4*>(p);
+        return *g;
 }
 
 template <bool NT>
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) {
+    TIDE_GLOBAL u32x4* g = (TIDE_GLOBAL u32x4*)(p);
     if constexpr (NT)
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+        __builtin_nontemporal_store(v, g);
     else
-        *reinterpret_cast<u32x4*>(p) = v;
+        *g = v;
 }
 
 constexpr int kUnroll = 4;  // 16-byte vectors in flight per lane
@@ -71,14 +76,16 @@ __device__ __forceinline__ void copy_vec16(const uint16_t* __restrict__ src,
 
 __device__ __forceinline__ void copy_vec4(const uint16_t* __restrict__ src,
                                           uint16_t* __restrict__ dst, int len) {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
-    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+    const TIDE_GLOBAL uint32_t* s = (const TIDE_GLOBAL uint32_t*)(src);
+    TIDE_GLOBAL uint32_t* d = (TIDE_GLOBAL uint32_t*)(dst);
     for (int e = threadIdx.x; e < len / 2; e += kBlock) d[e] = s[e];
 }
 
 __device__ __forceinline__ void copy_scalar(const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ dst, int len) {
-    for (int e = threadIdx.x; e < len; e += kBlock) dst[e] = src[e];
+    const TIDE_GLOBAL uint16_t* s = (const TIDE_GLOBAL uint16_t*)(src);
+    TIDE_GLOBAL uint16_t* d = (TIDE_GLOBAL uint16_t*)(dst);
+    for (int e = threadIdx.x; e < len; e += kBlock) d[e] = s[e];
 }
 
 template <bool NTL, bool NTS>
@@ -172,4 +179,27 @@ extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_onl
         }
     }
     return TIDE_OK;
+}
+
+extern "C" tide_status tide_stream_create_cu_limited(int32_t n_cu, tide_stream_t* out) {
+    if (!out || n_cu < 1) return TIDE_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TIDE_EHIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TIDE_EHIP;
+    const int ncu = prop.multiProcessorCount;
+    if (n_cu > ncu) return TIDE_EINVAL;
+    uint32_t mask[64] = {0};
+    const int words = (ncu + 31) / 32;
+    if (words > 64) return TIDE_EUNSUPPORTED;
+    for (int i = 0; i < n_cu; ++i) mask[i / 32] |= 1u << (i % 32);
+    hipStream_t s = nullptr;
+    if (hipExtStreamCreateWithCUMask(&s, (uint32_t)words, mask) != hipSuccess) return TIDE_EHIP;
+    *out = reinterpret_cast<tide_stream_t>(s);
+    return TIDE_OK;
+}
+
+extern "C" tide_status tide_stream_destroy(tide_stream_t stream) {
+    if (!stream) return TIDE_EINVAL;
+    return hipStreamDestroy(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? TIDE_OK : TIDE_EHIP;
 }

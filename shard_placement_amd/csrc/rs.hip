@@ -33,21 +33,33 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Every buffer the kernels touch is device global memory; saying so lets
+// the compiler emit global_* instead of flat_* memory instructions.
+#define TIDE_GLOBAL __attribute__((address_space(1)))
+
 template <bool NT>
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    const TIDE_GLOBAL u32x4* g = (const TIDE_GLOBAL u32x4*)(p);
     if constexpr (NT)
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return __builtin_nontemporal_load(g);
     else
-        return *reinterpret_cast<const u32x4*>(p);
+        return *g;
 }
 
 template <bool NT>
 __device__ __forceinline__ void store16(float* p, f32x4 v) {
+    TIDE_GLOBAL f32x4* g = (TIDE_GLOBAL f32x4*)(p);
     if constexpr (NT)
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+        __builtin_nontemporal_store(v, g);
     else
-        *reinterpret_cast<f32x4*>(p) = v;
+        *g = v;
 }
+
+__device__ __forceinline__ uint16_t load2(const uint16_t* p) {
+    return *(const TIDE_GLOBAL uint16_t*)(p);
+}
+
+__device__ __forceinline__ void store4(float* p, float v) { *(TIDE_GLOBAL float*)(p) = v; }
 
 // bf16 is the upper half of a binary32, so widening is a shift (exact).
 // A 32-bit word holds elements 2k (low half) and 2k+1 (high half).
@@ -74,43 +86,75 @@ __device__ __forceinline__ const uint16_t* src_of(const uint64_t* gp, int q) {
     return reinterpret_cast<const uint16_t*>(gp[q]);
 }
 
-// Vector tile, fixed rank order.  RB ranks are loaded per batch; EXACT means
-// R is a multiple of RB (no per-rank guard).  gp: the R source pointers of
-// this param (uniform); j0: first flat index; len % 8 == 0.
-template <int RB, bool EXACT, bool NTL, bool NTS>
+// Rank q's source at element j0 + e: a uniform 64-bit base plus a 32-bit
+// per-lane byte offset, so the loads use the scalar-base addressing form.
+__device__ __forceinline__ const uint16_t* at(const uint64_t* gp, int q, int64_t j0, int e) {
+    const char* base = reinterpret_cast<const char*>(gp[q]) + 2 * j0;
+    return reinterpret_cast<const uint16_t*>(base + (uint32_t)(2 * e));
+}
+
+// Vector tile, fixed rank order.  Each lane owns U chunks of 8 elements
+// (kBlock*8 apart) and issues U*RB 16-byte loads before it adds anything, so
+// about 16 loads are in flight per lane.  RB ranks are loaded per batch;
+// EXACT means R is a multiple of RB (no per-rank guard).  gp: the R source
+// pointers of this param (uniform); j0: first flat index; len % 8 == 0.
+template <int RB, bool EXACT, int U, bool NTL, bool NTS>
 __device__ __forceinline__ void rs_vec_fixed(const uint64_t* __restrict__ gp, int R, int64_t j0,
                                              int len, float* __restrict__ out) {
+    constexpr int kStep = kBlock * kVec;
     const bool out16 = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-    for (int e = threadIdx.x * kVec; e < len; e += kBlock * kVec) {
-        const int64_t j = j0 + e;
-        float a[8];
+    for (int base = threadIdx.x * kVec; base < len; base += kStep * U) {
+        float a[U][8];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ok[u] = base + u * kStep < len;
         {
-            u32x4 v[RB];
+            u32x4 v[U][RB];
             const int nb = EXACT ? RB : (R < RB ? R : RB);
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
-                if (EXACT || b < nb) v[b] = load16<NTL>(src_of(gp, b) + j);
-            acc_init(a, v[0]);
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int b = 1; b < RB; ++b)
-                if (EXACT || b < nb) acc_add(a, v[b]);
+                for (int b = 0; b < RB; ++b)
+                    if (ok[u] && (EXACT || b < nb))
+                        v[u][b] = load16<NTL>(at(gp, b, j0, base + u * kStep));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                acc_init(a[u], v[u][0]);
+#pragma unroll
+                for (int b = 1; b < RB; ++b)
+                    if (EXACT || b < nb) acc_add(a[u], v[u][b]);
+            }
         }
         for (int q0 = RB; q0 < R; q0 += RB) {
-            u32x4 v[RB];
+            u32x4 v[U][RB];
             const int nb = EXACT ? RB : ((R - q0) < RB ? (R - q0) : RB);
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
-                if (EXACT || b < nb) v[b] = load16<NTL>(src_of(gp, q0 + b) + j);
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
-                if (EXACT || b < nb) acc_add(a, v[b]);
+                for (int b = 0; b < RB; ++b)
+                    if (ok[u] && (EXACT || b < nb))
+                        v[u][b] = load16<NTL>(at(gp, q0 + b, j0, base + u * kStep));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+                    if (EXACT || b < nb) acc_add(a[u], v[u][b]);
+            }
         }
-        if (out16) {
-            store16<NTS>(out + e, f32x4{a[0], a[1], a[2], a[3]});
-            store16<NTS>(out + e + 4, f32x4{a[4], a[5], a[6], a[7]});
-        } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) out[e + k] = a[k];
+        for (int u = 0; u < U; ++u) {
+            if (!ok[u]) continue;
+            float* o = reinterpret_cast<float*>(reinterpret_cast<char*>(out) +
+                                                (uint32_t)(4 * (base + u * kStep)));
+            if (out16) {
+                store16<NTS>(o, f32x4{a[u][0], a[u][1], a[u][2], a[u][3]});
+                store16<NTS>(o + 4, f32x4{a[u][4], a[u][5], a[u][6], a[u][7]});
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) store4(o + k, a[u][k]);
+            }
         }
     }
 }
@@ -121,18 +165,145 @@ __device__ __forceinline__ void rs_scalar_fixed(const uint64_t* __restrict__ gp,
                                                 int len, float* __restrict__ out) {
     for (int e = threadIdx.x; e < len; e += kBlock) {
         const int64_t j = j0 + e;
-        float a = bf_one(src_of(gp, 0)[j]);
-        for (int q = 1; q < R; ++q) a = a + bf_one(src_of(gp, q)[j]);
-        out[e] = a;
+        float a = bf_one(load2(src_of(gp, 0) + j));
+        for (int q = 1; q < R; ++q) a = a + bf_one(load2(src_of(gp, q) + j));
+        store4(out + e, a);
     }
 }
 
 // Padding rows: +0.0f (all bits clear); nothing is read.
 __device__ __forceinline__ void rs_pad(int len, float* __restrict__ out) {
-    for (int e = threadIdx.x; e < len; e += kBlock) out[e] = 0.0f;
+    for (int e = threadIdx.x; e < len; e += kBlock) store4(out + e, 0.0f);
 }
 
-template <int RB, bool EXACT, bool NTL, bool NTS>
+// ---- tree order
+//
+// Pairwise over adjacent ranks, level by level, an odd last element carried
+// up unchanged.  That tree is the same as: split R ranks into a left block
+// of 2^k ranks (the largest power of two below R) and the rest, recursively;
+// i.e. perfect pairwise blocks of sizes given by R's binary digits, largest
+// first, combined right to left.  It is evaluated streaming, rank by rank,
+// as a binary counter: level l holds a finished block of 2^l ranks while
+// bit l of the count is set; pushing rank q merges (older block + newer)
+// for every trailing one of q.  Control flow depends only on the uniform
+// rank count, and every stack index is a compile-time constant, so the
+// stack stays in registers.  LEVELS >= floor(log2 R) + 1.
+template <int LEVELS, int W>
+struct TreeStack {
+    float v[LEVELS][W];
+
+    __device__ __forceinline__ void push(const float (&x_in)[W], int count) {
+        float x[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) x[k] = x_in[k];
+        bool placed = false;
+#pragma unroll
+        for (int l = 0; l < LEVELS; ++l) {
+            const bool carry = (count >> l) & 1;
+            if (!placed && carry) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) x[k] = v[l][k] + x[k];
+            }
+            if (!placed && !carry) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) v[l][k] = x[k];
+            }
+            placed = placed || !carry;
+        }
+    }
+
+    // After R pushes: combine the blocks named by R's set bits, smallest
+    // (rightmost ranks) first, each older block on the left.
+    __device__ __forceinline__ void finish(int R, float (&out)[W]) {
+        bool have = false;
+#pragma unroll
+        for (int l = 0; l < LEVELS; ++l) {
+            if ((R >> l) & 1) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) out[k] = have ? v[l][k] + out[k] : v[l][k];
+                have = true;
+            }
+        }
+    }
+};
+
+__device__ __forceinline__ void widen8(float (&x)[8], u32x4 v) {
+    x[0] = bf_lo(v.x); x[1] = bf_hi(v.x);
+    x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
+    x[4] = bf_lo(v.z); x[5] = bf_hi(v.z);
+    x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
+}
+
+template <int LEVELS, bool NTL, bool NTS>
+__device__ __forceinline__ void rs_vec_tree(const uint64_t* __restrict__ gp, int R, int64_t j0,
+                                            int len, float* __restrict__ out) {
+    constexpr int RB = 8;
+    const bool out16 = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    for (int e = threadIdx.x * kVec; e < len; e += kBlock * kVec) {
+        const int64_t j = j0 + e;
+        TreeStack<LEVELS, 8> st;
+        for (int q0 = 0; q0 < R; q0 += RB) {
+            u32x4 v[RB];
+            const int nb = (R - q0) < RB ? (R - q0) : RB;
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (b < nb) v[b] = load16<NTL>(src_of(gp, q0 + b) + j);
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (b < nb) {
+                    float x[8];
+                    widen8(x, v[b]);
+                    st.push(x, q0 + b);
+                }
+        }
+        float a[8];
+        st.finish(R, a);
+        if (out16) {
+            store16<NTS>(out + e, f32x4{a[0], a[1], a[2], a[3]});
+            store16<NTS>(out + e + 4, f32x4{a[4], a[5], a[6], a[7]});
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) store4(out + e + k, a[k]);
+        }
+    }
+}
+
+template <int LEVELS>
+__device__ __forceinline__ void rs_scalar_tree(const uint64_t* __restrict__ gp, int R, int64_t j0,
+                                               int len, float* __restrict__ out) {
+    for (int e = threadIdx.x; e < len; e += kBlock) {
+        const int64_t j = j0 + e;
+        TreeStack<LEVELS, 1> st;
+        for (int q = 0; q < R; ++q) {
+            float x[1] = {bf_one(load2(src_of(gp, q) + j))};
+            st.push(x, q);
+        }
+        float a[1];
+        st.finish(R, a);
+        store4(out + e, a[0]);
+    }
+}
+
+template <int LEVELS, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void rs_tree_kernel(const RsTile* __restrict__ tiles,
+                                                         int64_t ntiles,
+                                                         const uint64_t* __restrict__ gptr,
+                                                         const uint64_t* __restrict__ obase,
+                                                         int R) {
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const RsTile tile = tiles[t];
+        float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
+        const uint64_t* gp = gptr + (int64_t)tile.p * R;
+        if (tile.kind == kRsVec)
+            rs_vec_tree<LEVELS, NTL, NTS>(gp, R, tile.j0, tile.len, out);
+        else if (tile.kind == kRsScalar)
+            rs_scalar_tree<LEVELS>(gp, R, tile.j0, tile.len, out);
+        else
+            rs_pad(tile.len, out);
+    }
+}
+
+template <int RB, bool EXACT, int U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restrict__ tiles,
                                                           int64_t ntiles,
                                                           const uint64_t* __restrict__ gptr,
@@ -143,7 +314,7 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
         const uint64_t* gp = gptr + (int64_t)tile.p * R;
         if (tile.kind == kRsVec)
-            rs_vec_fixed<RB, EXACT, NTL, NTS>(gp, R, tile.j0, tile.len, out);
+            rs_vec_fixed<RB, EXACT, U, NTL, NTS>(gp, R, tile.j0, tile.len, out);
         else if (tile.kind == kRsScalar)
             rs_scalar_fixed(gp, R, tile.j0, tile.len, out);
         else
@@ -153,28 +324,46 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
 
 typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int);
 
-template <int RB, bool EXACT>
+template <int RB, bool EXACT, int U>
 RsKernel pick_nt(uint32_t flags) {
     const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
-    if (ntl && nts) return rs_fixed_kernel<RB, EXACT, true, true>;
-    if (ntl) return rs_fixed_kernel<RB, EXACT, true, false>;
-    if (nts) return rs_fixed_kernel<RB, EXACT, false, true>;
-    return rs_fixed_kernel<RB, EXACT, false, false>;
+    if (ntl && nts) return rs_fixed_kernel<RB, EXACT, U, true, true>;
+    if (ntl) return rs_fixed_kernel<RB, EXACT, U, true, false>;
+    if (nts) return rs_fixed_kernel<RB, EXACT, U, false, true>;
+    return rs_fixed_kernel<RB, EXACT, U, false, false>;
 }
 
-// Rank batching: small power-of-two R loads every rank at once; R a
-// multiple of 16 loads 16 per batch (64 VGPRs of loads in flight per lane);
-// anything else batches 8 with a guard.
+// Rank batching: small power-of-two R loads every rank at once (with U
+// chunks per lane when R < 8, so that at least 8 loads are in flight); R a
+// multiple of 16 loads 16 per batch (64 VGPRs of loads per lane); anything
+// else batches 8 with a guard.  Measured on MI355X: a second chunk per lane
+// at R = 8 did not help (5.6 vs 5.8 TB/s).
 RsKernel pick_fixed(int R, uint32_t flags) {
     switch (R) {
-        case 1: return pick_nt<1, true>(flags);
-        case 2: return pick_nt<2, true>(flags);
-        case 4: return pick_nt<4, true>(flags);
-        case 8: return pick_nt<8, true>(flags);
+        case 1: return pick_nt<1, true, 4>(flags);
+        case 2: return pick_nt<2, true, 4>(flags);
+        case 4: return pick_nt<4, true, 4>(flags);
+        case 8: return pick_nt<8, true, 1>(flags);
         default: break;
     }
-    if (R % 16 == 0) return pick_nt<16, true>(flags);
-    return pick_nt<8, false>(flags);
+    if (R % 16 == 0) return pick_nt<16, true, 1>(flags);
+    return pick_nt<8, false, 1>(flags);
+}
+
+template <int LEVELS>
+RsKernel pick_tree_nt(uint32_t flags) {
+    const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
+    if (ntl && nts) return rs_tree_kernel<LEVELS, true, true>;
+    if (ntl) return rs_tree_kernel<LEVELS, true, false>;
+    if (nts) return rs_tree_kernel<LEVELS, false, true>;
+    return rs_tree_kernel<LEVELS, false, false>;
+}
+
+// Stack depth: 7 levels hold blocks up to 64 ranks; 13 up to kMaxRanks.
+RsKernel pick_tree(int R, uint32_t flags) {
+    static_assert(kMaxRanks <= 4096, "13 levels cover R <= 8191");
+    if (R <= 127) return pick_tree_nt<7>(flags);
+    return pick_tree_nt<13>(flags);
 }
 
 }  // namespace
@@ -188,7 +377,6 @@ extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_pl
     if (order != 0 && order != 1) return TIDE_EINVAL;
     if (max_workgroups < 0) return TIDE_EINVAL;
     if (!h.has_rs) return TIDE_EUNSUPPORTED;
-    if (order != 0) return TIDE_EUNSUPPORTED;
     if (reinterpret_cast<uintptr_t>(d_plan) % 16) return TIDE_EALIGN;
     if (h.n_rs_tiles == 0) return TIDE_OK;
 
@@ -203,7 +391,7 @@ extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_pl
     if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
     if (grid > INT_MAX) grid = INT_MAX;
 
-    RsKernel k = pick_fixed(R, h.flags);
+    RsKernel k = order == 0 ? pick_fixed(R, h.flags) : pick_tree(R, h.flags);
     void* args[] = {&tiles, &ntiles, &gptr, &obase, &R};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
                                    dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));

@@ -1,0 +1,107 @@
+"""Interference probe: how much the reduce-scatter slows a concurrent GEMM.
+
+The paper reports that a default reduce-scatter can slow a concurrent GEMM
+that would otherwise finish in a single wave by 69%, and that TIDE cuts that
+interference by up to an order of magnitude (Abstract of "The Endgame of
+FSDP Communication", weekinpapers.com; kongchang.com article, sections "The
+Root of FSDP2 Communication Overhead" and "Performance").  This probe times a
+bf16 GEMM (torch.matmul -> hipBLASLt) alone, then beside a train of
+reduce-scatter launches on another stream, under several ways of confining
+the reduce-scatter: all CUs with one short-lived workgroup per tile, a capped
+grid of persistent workgroups, and a CU-masked stream.  The GEMM shape is
+chosen so that its grid is at most one workgroup per CU (checked with the
+rocprofv3 kernel trace).  It is a measurement: nothing here is parity.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import api
+
+DEFAULT_MODES: Tuple[Tuple[str, int, int], ...] = (
+    ("all-cus", 0, 0),
+    ("grid-256", 256, 0),
+    ("grid-128", 128, 0),
+    ("grid-64", 64, 0),
+    ("cu-mask-64", 0, 64),
+    ("cu-mask-32", 0, 32),
+)
+
+
+def _median(xs: List[float]) -> Optional[float]:
+    if not xs:
+        return None
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def _gemm_train(a, b, c, stream, n):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for e0, e1 in evs:
+            e0.record(stream)
+            torch.matmul(a, b, out=c)
+            e1.record(stream)
+    return evs
+
+
+def run(plan: "api.Plan", rs_bytes: int, modes: Sequence[Tuple[str, int, int]] = DEFAULT_MODES,
+        iters: int = 40, M: int = 4096, N: int = 4096, K: int = 8192) -> Dict:
+    dev = torch.device("cuda")
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    gemm_stream = torch.cuda.Stream()
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    alone = _gemm_train(a, b, c, gemm_stream, iters)
+    torch.cuda.synchronize()
+    t0 = _median([e0.elapsed_time(e1) for e0, e1 in alone])
+    out = {"gemm": "bf16 [%d,%d]x[%d,%d] torch.matmul" % (M, K, K, N),
+           "gemm_tflops_alone": round(2.0 * M * N * K / (t0 * 1e-3) / 1e12, 1),
+           "t_gemm_alone_ms": round(t0, 4), "modes": []}
+    for name, max_wg, n_cu in modes:
+        rs_stream = api.tide_stream_create_cu_limited(n_cu) if n_cu else torch.cuda.Stream()
+        try:
+            # reduce-scatter alone under this confinement
+            plan.rs(max_workgroups=max_wg, stream=rs_stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(rs_stream)
+            for _ in range(3):
+                plan.rs(max_workgroups=max_wg, stream=rs_stream)
+            e1.record(rs_stream)
+            torch.cuda.synchronize()
+            rs_alone = e0.elapsed_time(e1) / 3
+            # concurrent: enough reduce-scatters to cover the GEMM train twice
+            n_rs = max(2, int(2.0 * iters * t0 / rs_alone) + 2)
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record(rs_stream)
+            for _ in range(n_rs):
+                plan.rs(max_workgroups=max_wg, stream=rs_stream)
+            r1.record(rs_stream)
+            gemm_stream.wait_event(r0)
+            conc = _gemm_train(a, b, c, gemm_stream, iters)
+            torch.cuda.synchronize()
+            window = r0.elapsed_time(r1)
+            inside = [e1.elapsed_time(e2) for e1, e2 in conc
+                      if r0.elapsed_time(e1) >= 0.0 and r0.elapsed_time(e2) <= window]
+            t1 = _median(inside)
+            rs_conc = window / n_rs
+            out["modes"].append({
+                "mode": name, "max_workgroups": max_wg, "cu_mask": n_cu or None,
+                "rs_alone_ms": round(rs_alone, 4),
+                "rs_alone_gbps": round(rs_bytes / (rs_alone * 1e-3) / 1e9, 1),
+                "rs_concurrent_gbps": round(rs_bytes / (rs_conc * 1e-3) / 1e9, 1),
+                "t_gemm_concurrent_ms": round(t1, 4) if t1 else None,
+                "gemm_inside": len(inside),
+                "gemm_slowdown_pct": round(100.0 * (t1 / t0 - 1.0), 2) if t1 else None,
+            })
+        finally:
+            if n_cu:
+                torch.cuda.synchronize()
+                api.tide_stream_destroy(rs_stream)
+    return out

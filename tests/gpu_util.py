@@ -180,6 +180,8 @@ def check_rs_bound_all(st, order="fixed"):
                 absum += g.abs()
             err = (flat[a:b].to(torch.float64) - exact).abs()
             bad = err > gamma * absum * (1 + 1e-9) + 0.0
+            if order == "tree":
+                bad |= err > 1e-6 * absum
             assert not bool(bad.any()), "%s param %d: %d elements outside the bound" % (
                 w.name, p, int(bad.sum()))
 

@@ -33,13 +33,14 @@ def _run(st, order="fixed", max_wg=0):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("order", ["fixed", "tree"])
 @pytest.mark.parametrize("flags", [0, 1, 2, 3])
-def test_tiny_workload_bitwise(flags):
+def test_tiny_workload_bitwise(flags, order):
     w = configs.get(1)
-    gu.say("tiny rs flags", flags)
+    gu.say("tiny rs flags", flags, order)
     st = harness.setup(w, with_ag=False, gen_device="cpu", flags=flags)
-    _run(st)
-    gu.check_rs_full(st)
+    _run(st, order)
+    gu.check_rs_full(st, order)
 
 
 RANDOM_CASES = [
@@ -61,12 +62,24 @@ RANDOM_CASES = [
 
 @pytest.mark.parametrize("R,shapes", RANDOM_CASES, ids=[str(c[0]) for c in RANDOM_CASES])
 @pytest.mark.parametrize("tile", [0, 2048])
-def test_ragged_shapes_bitwise(R, shapes, tile):
+@pytest.mark.parametrize("order", ["fixed", "tree"])
+def test_ragged_shapes_bitwise(R, shapes, tile, order):
     w = _wl(shapes, R, key=100 + R)
-    gu.say("ragged rs R", R, shapes, "tile", tile)
+    gu.say("ragged rs R", R, shapes, "tile", tile, order)
     st = harness.setup(w, with_ag=False, rs_tile=tile)
-    _run(st)
-    gu.check_rs_full(st)
+    _run(st, order)
+    gu.check_rs_full(st, order)
+
+
+@pytest.mark.parametrize("R", [3, 5, 6, 7, 11, 13, 100, 129, 300])
+def test_tree_order_odd_rank_counts(R):
+    """Tree order for rank counts that are not powers of two (odd elements
+    carried up at several levels), including R > 127 (the deeper stack)."""
+    w = _wl([(R * 3 + 1, 24), (5,)], R, key=120 + R % 50)
+    gu.say("tree R", R)
+    st = harness.setup(w, with_ag=False, rs_tile=2048)
+    _run(st, "tree")
+    gu.check_rs_full(st, "tree")
 
 
 @pytest.mark.parametrize("align", [4, 8, 64])
@@ -140,12 +153,13 @@ def test_special_values():
 
 
 @pytest.mark.parametrize("max_wg", [1, 3, 64, 1000])
-def test_capped_grid_same_bits(max_wg):
+@pytest.mark.parametrize("order", ["fixed", "tree"])
+def test_capped_grid_same_bits(max_wg, order):
     w = _wl([(1001, 24), (5,), (64, 64)], 8, key=160)
-    gu.say("max_wg", max_wg)
+    gu.say("max_wg", max_wg, order)
     st = harness.setup(w, with_ag=False, rs_tile=2048)
-    _run(st, max_wg=max_wg)
-    gu.check_rs_full(st)
+    _run(st, order, max_wg=max_wg)
+    gu.check_rs_full(st, order)
 
 
 def test_deterministic_repeat():
@@ -241,6 +255,15 @@ def test_full_size_workload(key):
         gu.check_rs_by_param(st, [10, 11, 12])          # modulation (26 empty shards), norms
     if key == 5:
         gu.check_rs_by_param(st, [w.P - 1, 7])          # the ragged param, a norm
+    # tree order: sampled bit-exact vs the oracle's tree, and the tolerance
+    # 1e-6 * sum|g| (plus the pairwise bound) for every element
+    gu.say("tree order", w.name)
+    st.plan.rs(order="tree")
+    torch.cuda.synchronize()
+    gu.check_rs_sampled(st, order="tree", per_shard=32, edge=8, seed=1)
+    gu.check_rs_bound_all(st, order="tree")
+    st.plan.rs()
+    torch.cuda.synchronize()
     # determinism at full size
     snap = [o.clone() for o in st.out[:2]]
     st.plan.rs()
