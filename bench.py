@@ -116,6 +116,7 @@ def main():
     ap.add_argument("--workload", default="2", help="workload key or name (default: the Llama-3.1-70B layer, R=8)")
     ap.add_argument("--flags", type=int, default=-1, help="TIDE_FLAG_* access hints (-1: default)")
     ap.add_argument("--rs-tile", type=int, default=0)
+    ap.add_argument("--launch-mib", type=int, default=0, help="MiB per kernel launch (0: default, -1: one launch)")
     ap.add_argument("--ag-tile", type=int, default=0)
     ap.add_argument("--max-wg", type=int, default=0, help="cap the RS grid (0: one workgroup per tile)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
@@ -141,11 +142,14 @@ def main():
     w = configs.get(args.workload)
     log("workload", w.name, "R", w.R, "P", w.P, "N", w.numel())
     t0 = time.perf_counter()
-    st = harness.setup(w, guard=0, flags=args.flags, rs_tile=args.rs_tile, ag_tile=args.ag_tile)
+    st = harness.setup(w, guard=0, flags=args.flags, rs_tile=args.rs_tile, ag_tile=args.ag_tile,
+                       launch_mib=args.launch_mib)
     torch.cuda.synchronize()
-    log("setup %.1f s; plan: %d RS tiles of %d, %d AG tiles of %d, blob %d B" % (
-        time.perf_counter() - t0, st.plan.info.rs_tiles, st.plan.info.rs_tile_elems,
-        st.plan.info.ag_tiles, st.plan.info.ag_tile_elems, st.plan.info.blob_bytes))
+    info = st.plan.info
+    log("setup %.1f s; plan: %d RS tiles of %d (%d per launch), %d AG tiles of %d (%d per launch), "
+        "blob %d B" % (time.perf_counter() - t0, info.rs_tiles, info.rs_tile_elems,
+                       info.rs_launch_tiles, info.ag_tiles, info.ag_tile_elems,
+                       info.ag_launch_tiles, info.blob_bytes))
 
     if args.calib_copy_mib > 0:
         # a plain elementwise kernel of known traffic (reads and writes
@@ -209,7 +213,22 @@ def main():
     if args.probe:
         from shard_placement_amd import probe as probe_mod
 
-        probe = probe_mod.run(st.plan, rsb)
+        from shard_placement_amd import api as api_mod
+
+        def plan_with(mib):
+            return api_mod.Plan(w.shapes, w.R, grads=st.grads, out=st.out, flags=args.flags,
+                                rs_tile=args.rs_tile, launch_mib=mib)
+
+        one = plan_with(-1)
+        modes = [("default (%d MiB launches)" % (st.plan.info.rs_launch_tiles *
+                                                   st.plan.info.rs_tile_elems * (2 * w.R + 4) >> 20),
+                  st.plan, 0, 0),
+                 ("128 MiB launches", plan_with(128), 0, 0),
+                 ("64 MiB launches", plan_with(64), 0, 0),
+                 ("one launch", one, 0, 0),
+                 ("one launch, grid 256", one, 256, 0),
+                 ("one launch, CU mask 32", one, 0, 32)]
+        probe = probe_mod.run(modes, rsb)
         for m in probe["modes"]:
             log("probe", m)
 
@@ -244,6 +263,7 @@ def main():
         "ag_ms": round(ag_avg, 4),
         "ag_sdma": sdma,
         "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
+        "rs_launches": -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles))),
         "probe": probe,
         "roofline": {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rs_gbs / HBM_PEAK_GBS, 4),

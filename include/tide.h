@@ -92,7 +92,10 @@ typedef struct tide_opts {
                               (0: chosen from R, about 128 KB of traffic) */
     int32_t ag_tile_elems; /* elements per placement tile, multiple of 2048 (0: 2048) */
     int32_t flags;         /* -1: library default (both hints); else an OR of TIDE_FLAG_* */
-    int32_t reserved;      /* must be 0 */
+    int32_t launch_mib;    /* algorithmic MiB moved per kernel launch: a call is cut
+                              into launches of about this size, so that concurrent
+                              kernels on other streams get whole compute units at
+                              the launch boundaries (0: default 256; -1: one launch) */
 } tide_opts;
 
 /* Access hints (results are identical with any combination). */
@@ -109,6 +112,8 @@ typedef struct tide_plan_info {
     int64_t ag_tiles;       /* 0 when the plan has no placement pointers */
     int32_t rs_tile_elems, ag_tile_elems;
     int64_t blob_bytes;     /* bytes of the blob in use: upload this many */
+    int64_t rs_launch_tiles; /* tiles per reduce-scatter launch */
+    int64_t ag_launch_tiles; /* tiles per placement launch */
 } tide_plan_info;
 
 /* Size of the plan blob for these shapes (an upper bound that holds for
@@ -165,6 +170,19 @@ tide_status tide_plan_query(const void *h_plan, tide_plan_info *info);
 tide_status tide_rs_bf16_to_fp32(const void *h_plan, const void *d_plan,
                                  int32_t order, int32_t max_workgroups,
                                  tide_stream_t stream);
+
+/* The same reduce-scatter restricted to tiles [tile_begin, tile_begin +
+ * tile_count) of the plan (tide_plan_info.rs_tiles in all; tiles are in
+ * parameter order, then rank, then flat index).  Lets a caller cut one
+ * layer's reduce-scatter into several short launches, e.g. to leave the
+ * compute units to concurrent work between them, or to pipeline the
+ * gradient reads with a consumer of finished tiles [Abstract: a two-phase
+ * pipeline separates gradient reads from network progress].  A range past
+ * the end is TIDE_EINVAL; tile_count == 0 launches nothing. */
+tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
+                                       int32_t order, int64_t tile_begin,
+                                       int64_t tile_count, int32_t max_workgroups,
+                                       tide_stream_t stream);
 
 /* All-gather placement on the compute units [Abstract: TIDE-AG]: for
  * every param p and rank r, the clamp(d0 - r*s, 0, s) valid rows of slot r

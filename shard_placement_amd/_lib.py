@@ -21,7 +21,8 @@ FLAG_NT_STORES = 2
 # Every symbol include/tide.h declares.
 EXPORTS = ("tide_abi_version", "tide_status_str", "tide_desc_size", "tide_desc_geometry",
            "tide_desc_build", "tide_plan_query", "tide_rs_bf16_to_fp32", "tide_ag_place",
-           "tide_ag_place_sdma", "tide_stream_create_cu_limited", "tide_stream_destroy")
+           "tide_ag_place_sdma", "tide_stream_create_cu_limited", "tide_stream_destroy",
+           "tide_rs_bf16_to_fp32_tiles")
 
 
 class TideShape(ctypes.Structure):
@@ -31,7 +32,7 @@ class TideShape(ctypes.Structure):
 class TideOpts(ctypes.Structure):
     _fields_ = [("align_elems", ctypes.c_int64), ("rs_tile_elems", ctypes.c_int32),
                 ("ag_tile_elems", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("launch_mib", ctypes.c_int32)]
 
 
 class TidePlanInfo(ctypes.Structure):
@@ -39,7 +40,8 @@ class TidePlanInfo(ctypes.Structure):
                 ("slot_numel", ctypes.c_int64), ("numel", ctypes.c_int64),
                 ("padded_numel", ctypes.c_int64), ("rs_tiles", ctypes.c_int64),
                 ("ag_tiles", ctypes.c_int64), ("rs_tile_elems", ctypes.c_int32),
-                ("ag_tile_elems", ctypes.c_int32), ("blob_bytes", ctypes.c_int64)]
+                ("ag_tile_elems", ctypes.c_int32), ("blob_bytes", ctypes.c_int64),
+                ("rs_launch_tiles", ctypes.c_int64), ("ag_launch_tiles", ctypes.c_int64)]
 
 
 class TideError(RuntimeError):
@@ -86,13 +88,15 @@ def lib():
                                   ctypes.POINTER(TidePlanInfo)]
     L.tide_plan_query.argtypes = [vp, ctypes.POINTER(TidePlanInfo)]
     L.tide_rs_bf16_to_fp32.argtypes = [vp, vp, i32, i32, vp]
+    L.tide_rs_bf16_to_fp32_tiles.argtypes = [vp, vp, i32, i64, i64, i32, vp]
     L.tide_ag_place.argtypes = [vp, vp, i32, vp]
     L.tide_ag_place_sdma.argtypes = [vp, i32, vp]
     L.tide_stream_create_cu_limited.argtypes = [i32, ctypes.POINTER(vp)]
     L.tide_stream_destroy.argtypes = [vp]
     for name in ("tide_desc_size", "tide_desc_geometry", "tide_desc_build", "tide_plan_query",
                  "tide_rs_bf16_to_fp32", "tide_ag_place", "tide_ag_place_sdma",
-                 "tide_stream_create_cu_limited", "tide_stream_destroy"):
+                 "tide_stream_create_cu_limited", "tide_stream_destroy",
+                 "tide_rs_bf16_to_fp32_tiles"):
         getattr(L, name).restype = ctypes.c_int
     if L.tide_abi_version() != 1:
         raise RuntimeError("libtide ABI version %d, expected 1" % L.tide_abi_version())

@@ -40,8 +40,9 @@ def _shapes(shapes: Sequence[Sequence[int]]):
     return arr
 
 
-def _opts(align: int = 1, rs_tile: int = 0, ag_tile: int = 0, flags: int = -1) -> TideOpts:
-    return TideOpts(int(align), int(rs_tile), int(ag_tile), int(flags), 0)
+def _opts(align: int = 1, rs_tile: int = 0, ag_tile: int = 0, flags: int = -1,
+          launch_mib: int = 0) -> TideOpts:
+    return TideOpts(int(align), int(rs_tile), int(ag_tile), int(flags), int(launch_mib))
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -67,9 +68,9 @@ def tide_desc_geometry(shapes, R: int, align: int = 1) -> Tuple[np.ndarray, np.n
 
 
 def tide_desc_size(shapes, R: int, align: int = 1, rs_tile: int = 0, ag_tile: int = 0,
-                   flags: int = -1) -> int:
+                   flags: int = -1, launch_mib: int = 0) -> int:
     n = ctypes.c_size_t(0)
-    o = _opts(align, rs_tile, ag_tile, flags)
+    o = _opts(align, rs_tile, ag_tile, flags, launch_mib)
     check(_lib.lib().tide_desc_size(_shapes(shapes), len(shapes), int(R), ctypes.byref(o),
                                     ctypes.byref(n)), "tide_desc_size")
     return int(n.value)
@@ -77,12 +78,12 @@ def tide_desc_size(shapes, R: int, align: int = 1, rs_tile: int = 0, ag_tile: in
 
 def tide_desc_build(shapes, R: int, grad_ptrs=None, out_ptrs=None, gathered_ptr=None,
                     full_ptrs=None, align: int = 1, rs_tile: int = 0, ag_tile: int = 0,
-                    flags: int = -1) -> Tuple[np.ndarray, TidePlanInfo]:
+                    flags: int = -1, launch_mib: int = 0) -> Tuple[np.ndarray, TidePlanInfo]:
     """Build a host plan blob from raw device addresses (ints).  grad_ptrs is
     rank-major [R*P]; out_ptrs [R]; full_ptrs [P].  Returns (blob, info)."""
     L = _lib.lib()
     P = len(shapes)
-    size = tide_desc_size(shapes, R, align, rs_tile, ag_tile, flags)
+    size = tide_desc_size(shapes, R, align, rs_tile, ag_tile, flags, launch_mib)
     blob = np.zeros(size, np.uint8)
     vp = ctypes.c_void_p
 
@@ -95,7 +96,7 @@ def tide_desc_build(shapes, R: int, grad_ptrs=None, out_ptrs=None, gathered_ptr=
         return a
 
     info = TidePlanInfo()
-    o = _opts(align, rs_tile, ag_tile, flags)
+    o = _opts(align, rs_tile, ag_tile, flags, launch_mib)
     st = L.tide_desc_build(_shapes(shapes), P, int(R), ctypes.byref(o), arr(grad_ptrs, R * P),
                            arr(out_ptrs, R), vp(int(gathered_ptr)) if gathered_ptr else None,
                            arr(full_ptrs, P), blob.ctypes.data, blob.nbytes, ctypes.byref(info))
@@ -108,6 +109,15 @@ def tide_rs_bf16_to_fp32(h_plan: np.ndarray, d_plan: torch.Tensor, order: int = 
     check(_lib.lib().tide_rs_bf16_to_fp32(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
                                           int(max_workgroups), _stream(stream)),
           "tide_rs_bf16_to_fp32")
+
+
+def tide_rs_bf16_to_fp32_tiles(h_plan: np.ndarray, d_plan: torch.Tensor, order: int,
+                               tile_begin: int, tile_count: int, max_workgroups: int = 0,
+                               stream=None) -> None:
+    check(_lib.lib().tide_rs_bf16_to_fp32_tiles(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
+                                                int(tile_begin), int(tile_count),
+                                                int(max_workgroups), _stream(stream)),
+          "tide_rs_bf16_to_fp32_tiles")
 
 
 def tide_ag_place(h_plan: np.ndarray, d_plan: torch.Tensor, max_workgroups: int = 0,
@@ -157,7 +167,8 @@ class Plan:
     """
 
     def __init__(self, shapes, R: int, grads=None, out=None, gathered=None, full=None,
-                 align: int = 1, rs_tile: int = 0, ag_tile: int = 0, flags: int = -1):
+                 align: int = 1, rs_tile: int = 0, ag_tile: int = 0, flags: int = -1,
+                 launch_mib: int = 0):
         self.shapes = [tuple(int(d) for d in s) for s in shapes]
         self.R = int(R)
         self.P = len(self.shapes)
@@ -205,7 +216,8 @@ class Plan:
         if device is None:
             raise TideError(-1, "a plan needs gradients or a gathered buffer")
         self.blob, self.info = tide_desc_build(self.shapes, self.R, grad_ptrs, out_ptrs, gptr,
-                                               full_ptrs, align, rs_tile, ag_tile, flags)
+                                               full_ptrs, align, rs_tile, ag_tile, flags,
+                                               launch_mib)
         used = int(self.info.blob_bytes)
         self.blob = self.blob[:used].copy()
         self.d_blob = torch.from_numpy(self.blob).to(device)
@@ -213,6 +225,18 @@ class Plan:
 
     def rs(self, order: str = "fixed", max_workgroups: int = 0, stream=None) -> None:
         tide_rs_bf16_to_fp32(self.blob, self.d_blob, ORDERS[order], max_workgroups, stream)
+
+    def rs_chunked(self, chunk_tiles: int, order: str = "fixed", max_workgroups: int = 0,
+                   stream=None) -> int:
+        """The reduce-scatter as ceil(rs_tiles / chunk_tiles) launches of at
+        most chunk_tiles tiles each; returns the number of launches."""
+        n = int(self.info.rs_tiles)
+        launches = 0
+        for b in range(0, n, chunk_tiles):
+            tide_rs_bf16_to_fp32_tiles(self.blob, self.d_blob, ORDERS[order], b,
+                                       min(chunk_tiles, n - b), max_workgroups, stream)
+            launches += 1
+        return launches
 
     def ag(self, max_workgroups: int = 0, stream=None) -> None:
         tide_ag_place(self.blob, self.d_blob, max_workgroups, stream)

@@ -130,20 +130,24 @@ extern "C" tide_status tide_ag_place(const void* h_plan, const void* d_plan,
     if (h.n_ag_tiles == 0) return TIDE_OK;
 
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
-    const AgTile* tiles = reinterpret_cast<const AgTile*>(d + h.off_ag);
+    const AgTile* all = reinterpret_cast<const AgTile*>(d + h.off_ag);
     const uint64_t* full = reinterpret_cast<const uint64_t*>(d + h.off_full);
     const uint16_t* gathered = reinterpret_cast<const uint16_t*>(h.gathered);
-    int64_t ntiles = h.n_ag_tiles;
-
-    int64_t grid = ntiles;
-    if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
-    if (grid > INT_MAX) grid = INT_MAX;
-
     AgKernel k = pick(h.flags);
-    void* args[] = {&tiles, &ntiles, &gathered, &full};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
-                                   dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TIDE_OK : TIDE_EHIP;
+    const int64_t per_launch = h.ag_launch_tiles > 0 ? h.ag_launch_tiles : h.n_ag_tiles;
+
+    for (int64_t b = 0; b < h.n_ag_tiles; b += per_launch) {
+        const AgTile* tiles = all + b;
+        int64_t ntiles = per_launch < h.n_ag_tiles - b ? per_launch : h.n_ag_tiles - b;
+        int64_t grid = ntiles;
+        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+        if (grid > INT_MAX) grid = INT_MAX;
+        void* args[] = {&tiles, &ntiles, &gathered, &full};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return TIDE_EHIP;
+    }
+    return TIDE_OK;
 }
 
 extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_only,

@@ -40,10 +40,19 @@ int32_t default_rs_tile(int32_t R) {
 constexpr int32_t kDefaultAgTile = 2048;
 constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 
+// Launch granularity: about 256 MiB of algorithmic traffic per kernel
+// launch.  Measured on MI355X next to a single-wave bf16 GEMM on another
+// hardware queue: one launch for a whole layer starves the GEMM (it waits
+// for free compute units that the stream of short workgroups never leaves);
+// launch boundaries every 64-256 MiB let it in with <5% slowdown, for 2-4%
+// less reduce-scatter bandwidth alone.
+constexpr int32_t kDefaultLaunchMiB = 256;
+
 struct Resolved {
     int64_t align;
     int32_t rs_tile, ag_tile;
     uint32_t flags;
+    int64_t launch_bytes;  // <= 0: unlimited
 };
 
 tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
@@ -51,8 +60,11 @@ tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
     out->rs_tile = default_rs_tile(R);
     out->ag_tile = kDefaultAgTile;
     out->flags = kDefaultFlags;
+    out->launch_bytes = (int64_t)kDefaultLaunchMiB << 20;
     if (!o) return TIDE_OK;
-    if (o->reserved != 0) return TIDE_EINVAL;
+    if (o->launch_mib < -1 || o->launch_mib > (1 << 20)) return TIDE_EINVAL;
+    if (o->launch_mib == -1) out->launch_bytes = 0;
+    if (o->launch_mib > 0) out->launch_bytes = (int64_t)o->launch_mib << 20;
     if (o->align_elems < 1 || o->align_elems > (int64_t)1 << 20) return TIDE_EINVAL;
     out->align = o->align_elems;
     if (o->rs_tile_elems != 0) {
@@ -387,6 +399,15 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     }
 
     Layout L = section_layout(P, R, (int64_t)rs.size(), (int64_t)ag.size());
+    // tiles per launch from the launch size and each tile's traffic
+    const int64_t rs_tile_bytes = (int64_t)o.rs_tile * (2 * (int64_t)R + 4);
+    const int64_t ag_tile_bytes = (int64_t)o.ag_tile * 4;
+    int64_t rs_launch = std::max<int64_t>(1, (int64_t)rs.size());
+    int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
+    if (o.launch_bytes > 0) {
+        rs_launch = std::min(rs_launch, std::max<int64_t>(1, o.launch_bytes / rs_tile_bytes));
+        ag_launch = std::min(ag_launch, std::max<int64_t>(1, o.launch_bytes / ag_tile_bytes));
+    }
     if (info) {
         std::memset(info, 0, sizeof(*info));
         info->R = R;
@@ -399,6 +420,8 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
         info->rs_tile_elems = o.rs_tile;
         info->ag_tile_elems = o.ag_tile;
         info->blob_bytes = (int64_t)L.bytes;
+        info->rs_launch_tiles = rs_launch;
+        info->ag_launch_tiles = ag_launch;
     }
     if (blob_bytes < L.bytes) return TIDE_ENOSPACE;
 
@@ -429,6 +452,8 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     h.has_rs = has_rs ? 1 : 0;
     h.has_ag = has_ag ? 1 : 0;
     h.flags = o.flags;
+    h.rs_launch_tiles = rs_launch;
+    h.ag_launch_tiles = ag_launch;
     std::memcpy(b, &h, sizeof h);
     if (P) std::memcpy(b + L.off_params, ps.data(), sizeof(ParamDesc) * (size_t)P);
     uint64_t* gp = reinterpret_cast<uint64_t*>(b + L.off_gptr);
@@ -463,6 +488,8 @@ tide_status tide_plan_query(const void* h_plan, tide_plan_info* info) {
     info->rs_tile_elems = h.rs_tile;
     info->ag_tile_elems = h.ag_tile;
     info->blob_bytes = (int64_t)h.bytes;
+    info->rs_launch_tiles = h.rs_launch_tiles;
+    info->ag_launch_tiles = h.ag_launch_tiles;
     return TIDE_OK;
 }
 

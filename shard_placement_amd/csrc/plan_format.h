@@ -52,6 +52,8 @@ struct PlanHeader {
     int32_t has_ag;
     uint32_t flags;
     uint32_t reserved;
+    int64_t rs_launch_tiles;  // tiles per reduce-scatter kernel launch
+    int64_t ag_launch_tiles;  // tiles per placement kernel launch
 };
 
 struct ParamDesc {

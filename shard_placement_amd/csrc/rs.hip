@@ -368,8 +368,10 @@ RsKernel pick_tree(int R, uint32_t flags) {
 
 }  // namespace
 
-extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_plan, int32_t order,
-                                            int32_t max_workgroups, tide_stream_t stream) {
+namespace {
+
+tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int64_t tile_begin,
+                      int64_t tile_count, int32_t max_workgroups, tide_stream_t stream) {
     if (!h_plan || !d_plan) return TIDE_EINVAL;
     PlanHeader h;
     std::memcpy(&h, h_plan, sizeof h);
@@ -378,22 +380,48 @@ extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_pl
     if (max_workgroups < 0) return TIDE_EINVAL;
     if (!h.has_rs) return TIDE_EUNSUPPORTED;
     if (reinterpret_cast<uintptr_t>(d_plan) % 16) return TIDE_EALIGN;
-    if (h.n_rs_tiles == 0) return TIDE_OK;
+    if (tile_count < 0) tile_count = h.n_rs_tiles - tile_begin;
+    if (tile_begin < 0 || tile_count < 0 || tile_begin > h.n_rs_tiles ||
+        tile_count > h.n_rs_tiles - tile_begin)
+        return TIDE_EINVAL;
+    if (tile_count == 0) return TIDE_OK;
 
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
-    const RsTile* tiles = reinterpret_cast<const RsTile*>(d + h.off_rs);
+    const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
-    int64_t ntiles = h.n_rs_tiles;
     int R = h.R;
-
-    int64_t grid = ntiles;
-    if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
-    if (grid > INT_MAX) grid = INT_MAX;
-
     RsKernel k = order == 0 ? pick_fixed(R, h.flags) : pick_tree(R, h.flags);
-    void* args[] = {&tiles, &ntiles, &gptr, &obase, &R};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
-                                   dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TIDE_OK : TIDE_EHIP;
+    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
+
+    // One launch per run of per_launch tiles: the launch boundaries are where
+    // kernels on other hardware queues get whole compute units.
+    for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
+        const RsTile* tiles = all + b;
+        int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch
+                                                                  : tile_begin + tile_count - b;
+        int64_t grid = ntiles;
+        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+        if (grid > INT_MAX) grid = INT_MAX;
+        void* args[] = {&tiles, &ntiles, &gptr, &obase, &R};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return TIDE_EHIP;
+    }
+    return TIDE_OK;
+}
+
+}  // namespace
+
+extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_plan, int32_t order,
+                                            int32_t max_workgroups, tide_stream_t stream) {
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream);
+}
+
+extern "C" tide_status tide_rs_bf16_to_fp32_tiles(const void* h_plan, const void* d_plan,
+                                                  int32_t order, int64_t tile_begin,
+                                                  int64_t tile_count, int32_t max_workgroups,
+                                                  tide_stream_t stream) {
+    if (tile_count < 0) return TIDE_EINVAL;
+    return launch_rs(h_plan, d_plan, order, tile_begin, tile_count, max_workgroups, stream);
 }

@@ -54,7 +54,8 @@ def ag_bytes(w: configs.Workload) -> int:
 
 def setup(w: configs.Workload, device="cuda", with_rs=True, with_ag=True, guard: int = 256,
           slot_reuse: Optional[bool] = None, same_for_all: bool = False, align: int = 1,
-          rs_tile: int = 0, ag_tile: int = 0, flags: int = -1, gen_device=None) -> Setup:
+          rs_tile: int = 0, ag_tile: int = 0, flags: int = -1, gen_device=None,
+          launch_mib: int = 0) -> Setup:
     """Allocate and fill one workload.  Output arenas carry `guard` NaN-filled
     floats on each side (canaries).  With Slot-Reuse, rank r's fp32 arena is
     placed at byte 0 of rank r's own vacated gathered buffer (2*R*S bytes,
@@ -110,5 +111,5 @@ def setup(w: configs.Workload, device="cuda", with_rs=True, with_ag=True, guard:
     st.plan = api.Plan(w.shapes, w.R,
                        grads=st.grads if with_rs else None, out=st.out if with_rs else None,
                        gathered=st.gathered, full=st.full, align=align, rs_tile=rs_tile,
-                       ag_tile=ag_tile, flags=flags)
+                       ag_tile=ag_tile, flags=flags, launch_mib=launch_mib)
     return st

@@ -8,7 +8,8 @@ Root of FSDP2 Communication Overhead" and "Performance").  This probe times a
 bf16 GEMM (torch.matmul -> hipBLASLt) alone, then beside a train of
 reduce-scatter launches on another stream, under several ways of confining
 the reduce-scatter: all CUs with one short-lived workgroup per tile, a capped
-grid of persistent workgroups, and a CU-masked stream.  The GEMM shape is
+grid of persistent workgroups, a CU-masked stream, and the launch size (a
+call cut into launches of about launch_mib MiB each).  The GEMM shape is
 chosen so that its grid is at most one workgroup per CU (checked with the
 rocprofv3 kernel trace).  It is a measurement: nothing here is parity.
 """
@@ -20,14 +21,8 @@ import torch
 
 from . import api
 
-DEFAULT_MODES: Tuple[Tuple[str, int, int], ...] = (
-    ("all-cus", 0, 0),
-    ("grid-256", 256, 0),
-    ("grid-128", 128, 0),
-    ("grid-64", 64, 0),
-    ("cu-mask-64", 0, 64),
-    ("cu-mask-32", 0, 32),
-)
+# A mode: (name, plan, max_workgroups, CU-mask width); 0 = unlimited / all.
+Mode = Tuple[str, "api.Plan", int, int]
 
 
 def _median(xs: List[float]) -> Optional[float]:
@@ -48,9 +43,15 @@ def _gemm_train(a, b, c, stream, n):
     return evs
 
 
-def run(plan: "api.Plan", rs_bytes: int, modes: Sequence[Tuple[str, int, int]] = DEFAULT_MODES,
-        iters: int = 40, M: int = 4096, N: int = 4096, K: int = 8192) -> Dict:
+def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N: int = 4096,
+        K: int = 8192) -> Dict:
+    """Time the GEMM alone, then beside each mode's reduce-scatter.  The
+    reduce-scatter always runs on a CU-masked stream, which HIP backs with a
+    hardware queue of its own (with the full mask when the mode has none):
+    two streams that share a hardware queue run one after the other, which
+    would hide any interference."""
     dev = torch.device("cuda")
+    n_all = torch.cuda.get_device_properties(dev).multi_processor_count
     a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
     b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
     c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
@@ -63,11 +64,10 @@ def run(plan: "api.Plan", rs_bytes: int, modes: Sequence[Tuple[str, int, int]] =
     t0 = _median([e0.elapsed_time(e1) for e0, e1 in alone])
     out = {"gemm": "bf16 [%d,%d]x[%d,%d] torch.matmul" % (M, K, K, N),
            "gemm_tflops_alone": round(2.0 * M * N * K / (t0 * 1e-3) / 1e12, 1),
-           "t_gemm_alone_ms": round(t0, 4), "modes": []}
-    for name, max_wg, n_cu in modes:
-        rs_stream = api.tide_stream_create_cu_limited(n_cu) if n_cu else torch.cuda.Stream()
+           "t_gemm_alone_ms": round(t0, 4), "cus": n_all, "modes": []}
+    for name, plan, max_wg, n_cu in modes:
+        rs_stream = api.tide_stream_create_cu_limited(n_cu or n_all)
         try:
-            # reduce-scatter alone under this confinement
             plan.rs(max_workgroups=max_wg, stream=rs_stream)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(rs_stream)
@@ -91,17 +91,20 @@ def run(plan: "api.Plan", rs_bytes: int, modes: Sequence[Tuple[str, int, int]] =
                       if r0.elapsed_time(e1) >= 0.0 and r0.elapsed_time(e2) <= window]
             t1 = _median(inside)
             rs_conc = window / n_rs
+            info = plan.info
             out["modes"].append({
-                "mode": name, "max_workgroups": max_wg, "cu_mask": n_cu or None,
+                "mode": name, "max_workgroups": max_wg or None, "cu_mask": n_cu or None,
+                "tiles_per_launch": int(info.rs_launch_tiles),
+                "launches_per_rs": -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles))),
                 "rs_alone_ms": round(rs_alone, 4),
                 "rs_alone_gbps": round(rs_bytes / (rs_alone * 1e-3) / 1e9, 1),
                 "rs_concurrent_gbps": round(rs_bytes / (rs_conc * 1e-3) / 1e9, 1),
                 "t_gemm_concurrent_ms": round(t1, 4) if t1 else None,
                 "gemm_inside": len(inside),
-                "gemm_slowdown_pct": round(100.0 * (t1 / t0 - 1.0), 2) if t1 else None,
+                # no GEMM inside the window: it waited for the whole train
+                "gemm_slowdown_pct": round(100.0 * (t1 / t0 - 1.0), 2) if t1 else "starved",
             })
         finally:
-            if n_cu:
-                torch.cuda.synchronize()
-                api.tide_stream_destroy(rs_stream)
+            torch.cuda.synchronize()
+            api.tide_stream_destroy(rs_stream)
     return out

@@ -22,7 +22,7 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("R", "<i4"), ("P", "<i4")
                 ("off_params", "<u8"), ("off_gptr", "<u8"), ("off_obase", "<u8"),
                 ("off_full", "<u8"), ("off_rs", "<u8"), ("off_ag", "<u8"),
                 ("gathered", "<u8"), ("bytes", "<u8"), ("has_rs", "<i4"), ("has_ag", "<i4"),
-                ("flags", "<u4"), ("reserved", "<u4")])
+                ("flags", "<u4"), ("reserved", "<u4"), ("rs_launch", "<i8"), ("ag_launch", "<i8")])
 RS_TILE = np.dtype([("j0", "<i8"), ("o0", "<i8"), ("p", "<i4"), ("r", "<i4"),
                     ("len", "<i4"), ("kind", "<i4")])
 AG_TILE = np.dtype([("src", "<i8"), ("dst", "<i8"), ("p", "<i4"), ("len", "<i4"),
@@ -262,5 +262,28 @@ def test_launches_reject_before_touching_the_gpu():
     assert L.tide_plan_query(junk.ctypes.data, ctypes.byref(info)) == -7
     assert L.tide_plan_query(blob.ctypes.data, ctypes.byref(info)) == 0
     assert info.R == R and info.slot_numel == S
+    n_rs = int(np.frombuffer(blob[:HDR.itemsize].tobytes(), HDR)[0]["n_rs"])
+    T = L.tide_rs_bf16_to_fp32_tiles
+    assert T(blob.ctypes.data, fake_dev, 0, 0, n_rs + 1, 0, None) == -1          # past the end
+    assert T(blob.ctypes.data, fake_dev, 0, n_rs, 1, 0, None) == -1
+    assert T(blob.ctypes.data, fake_dev, 0, -1, 1, 0, None) == -1
+    assert T(blob.ctypes.data, fake_dev, 0, 0, -1, 0, None) == -1
+    assert T(blob.ctypes.data, fake_dev, 0, n_rs, 0, 0, None) == 0              # empty range
     ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
     assert L.tide_rs_bf16_to_fp32(ag_blob.ctypes.data, fake_dev, 0, 0, None) == -6
+
+
+def test_launch_granularity():
+    shapes = [(8192, 1024), (100, 7)]
+    R = 8
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    g, o, ga, f = _fake_ptrs(shapes, R, S)
+    _, info = api.tide_desc_build(shapes, R, g, o, ga, f)
+    per_tile = info.rs_tile_elems * (2 * R + 4)
+    assert info.rs_launch_tiles == min(info.rs_tiles, (256 << 20) // per_tile)
+    assert info.ag_launch_tiles == min(info.ag_tiles, (256 << 20) // (info.ag_tile_elems * 4))
+    _, one = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=-1)
+    assert one.rs_launch_tiles == one.rs_tiles and one.ag_launch_tiles == one.ag_tiles
+    _, small = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=1)
+    assert small.rs_launch_tiles == max(1, (1 << 20) // per_tile)
+    assert _status(api.tide_desc_build, shapes, R, g, o, ga, f, 1, 0, 0, -1, -2) == -1

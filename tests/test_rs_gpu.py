@@ -162,6 +162,31 @@ def test_capped_grid_same_bits(max_wg, order):
     gu.check_rs_full(st, order)
 
 
+@pytest.mark.parametrize("chunk", [1, 7, 64])
+def test_chunked_launches_same_bits(chunk):
+    """The reduce-scatter cut into tile ranges gives the same bits."""
+    w = _wl([(1001, 24), (5,), (64, 64)], 8, key=165)
+    st = harness.setup(w, with_ag=False, rs_tile=2048)
+    n = st.plan.rs_chunked(chunk)
+    torch.cuda.synchronize()
+    assert n == -(-int(st.plan.info.rs_tiles) // chunk)
+    gu.check_rs_full(st)
+
+
+@pytest.mark.parametrize("launch_mib", [-1, 1, 4])
+def test_launch_size_same_bits(launch_mib):
+    """A call cut into many launches (or made in one) gives the same bits;
+    so does the placement."""
+    w = _wl([(1001, 96), (5,), (640, 64)], 8, key=166)
+    st = harness.setup(w, rs_tile=2048, ag_tile=2048, launch_mib=launch_mib)
+    assert st.plan.info.rs_launch_tiles >= 1
+    st.plan.rs()
+    st.plan.ag()
+    torch.cuda.synchronize()
+    gu.check_rs_full(st)
+    gu.check_ag_full(st)
+
+
 def test_deterministic_repeat():
     w = _wl([(4096, 256), (7,)], 16, key=170, sigma=1e-3)
     st = harness.setup(w, with_ag=False)
