@@ -232,13 +232,17 @@ def main():
         for m in probe["modes"]:
             log("probe", m)
 
-    traffic = read_traffic("rs", w.name, RS_SOURCES)
+    traffic = read_traffic("rs_fixed_kernel", w.name, RS_SOURCES)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host cores")
         cpu = cpu_baseline(st, args.cpu_budget)
         log("cpu baseline", cpu)
 
+    n_launch = -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles)))
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = int(info.rs_launch_tiles) if args.max_wg == 0 else min(args.max_wg, int(info.rs_launch_tiles))
+    rs_cus = min(grid, n_cus)  # workgroups spread over every CU when the grid exceeds them
     rec = {
         "metric": "RS bf16->fp32 shard GB/s & % of HBM peak; AG placement GB/s; GEMM slowdown %",
         "value": round((rsb + agb) / (ms_step * 1e-3) / 1e9, 1),
@@ -263,12 +267,21 @@ def main():
         "ag_ms": round(ag_avg, 4),
         "ag_sdma": sdma,
         "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
-        "rs_launches": -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles))),
+        "rs_launches": n_launch,
+        "rs_cus": rs_cus,
+        "rs_cu_ms": round(rs_cus * rs_avg, 1),
         "probe": probe,
+        # per kernel launch: one reduce-scatter call is n_launch launches of
+        # about rsb / n_launch algorithmic bytes; the event time per call
+        # (divided by n_launch) includes the short gaps between launches
         "roofline": {"bound": "hbm", "achieved": round(rs_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rs_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "rs_fixed_kernel",
-                     "algorithmic_bytes_per_launch": rsb},
+                     "launches_per_call": n_launch,
+                     "algorithmic_bytes_per_launch": rsb // n_launch,
+                     "avg_launch_ms": round(rs_avg / n_launch, 5),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, "
+                                     "copy-calibrated)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
