@@ -206,7 +206,7 @@ def main():
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / reps
         sdma = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
-                "engine": "hipMemcpyDeviceToDeviceNoCU copies (2-D per param + 1-D partial rank)"}
+                "engine": "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run"}
         log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
 
     probe = None

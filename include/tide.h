@@ -191,14 +191,23 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
 tide_status tide_ag_place(const void *h_plan, const void *d_plan,
                           int32_t max_workgroups, tide_stream_t stream);
 
-/* The same placement issued as copies on the DMA (copy) engines, with no
- * compute-unit kernel [Abstract: no SMs used for placement]: at most two
- * copies per param (a 2-D copy over the ranks with full shards, a 1-D copy
- * for the one partial rank), issued from the host plan, asynchronous on
- * `stream`.  engine_only = 1 requests the runtime's no-compute-unit copy
- * kind; 0 lets the runtime choose. */
+/* The same placement issued as host-side copies from the host plan,
+ * asynchronous on `stream` [Abstract: no SMs used for placement].
+ * engine_only = 1: one 1-D copy per (param, rank) run with the runtime's
+ * no-compute-unit copy kind (hipMemcpyDeviceToDeviceNoCU): the DMA engines
+ * move the data, no kernel runs.  engine_only = 0: at most two copies per
+ * param (a 2-D copy over the ranks with full shards, a 1-D copy for the
+ * partial rank) of the ordinary device-to-device kind, which the runtime
+ * executes with a blit kernel. */
 tide_status tide_ag_place_sdma(const void *h_plan, int32_t engine_only,
                                tide_stream_t stream);
+
+/* The engine-only placement with its copies spread over n_streams streams
+ * (largest first, each to the stream with the fewest bytes so far), so
+ * that several DMA engines can work at once.  The caller orders the
+ * streams against its other work (e.g. with events); no kernel runs. */
+tide_status tide_ag_place_sdma_streams(const void *h_plan, const tide_stream_t *streams,
+                                       int32_t n_streams);
 
 /* A stream whose kernels may run only on the first n_cu compute units of
  * the device's CU mask (hipExtStreamCreateWithCUMask; default priority), for

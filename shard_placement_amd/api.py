@@ -131,6 +131,12 @@ def tide_ag_place_sdma(h_plan: np.ndarray, engine_only: bool = True, stream=None
                                         _stream(stream)), "tide_ag_place_sdma")
 
 
+def tide_ag_place_sdma_streams(h_plan: np.ndarray, streams) -> None:
+    arr = (ctypes.c_void_p * len(streams))(*[int(s.cuda_stream) for s in streams])
+    check(_lib.lib().tide_ag_place_sdma_streams(h_plan.ctypes.data, arr, len(streams)),
+          "tide_ag_place_sdma_streams")
+
+
 def tide_stream_create_cu_limited(n_cu: int) -> torch.cuda.ExternalStream:
     """A torch stream wrapping a HIP stream confined to the first n_cu CUs.
     Release it with tide_stream_destroy."""
@@ -243,6 +249,11 @@ class Plan:
 
     def ag_sdma(self, engine_only: bool = True, stream=None) -> None:
         tide_ag_place_sdma(self.blob, engine_only, stream)
+
+    def ag_sdma_streams(self, streams) -> None:
+        """Engine-only placement spread over several streams.  The caller
+        orders them against other work (e.g. with events)."""
+        tide_ag_place_sdma_streams(self.blob, streams)
 
     def shard(self, out_arena: torch.Tensor, p: int) -> torch.Tensor:
         """View of param p's shard in one rank's fp32 arena, shaped [s, rest...]."""

@@ -14,14 +14,20 @@
 //                       of up to ag_tile elements; 16-byte loads and stores
 //                       where both ends allow it (4 vectors in flight per
 //                       lane), 4-byte or 2-byte moves otherwise.
-//   tide_ag_place_sdma  host-issued copies on the DMA engines, no compute
-//                       units ("no SMs used for transport or placement",
-//                       same Abstract): one 2-D copy over the ranks whose
-//                       shard is full, one 1-D copy for the partial rank.
+//   tide_ag_place_sdma  host-issued copies.  engine_only = 1: one 1-D copy
+//                       per (param, rank) run with the no-compute-unit copy
+//                       kind, executed by the DMA engines ("no SMs used for
+//                       transport or placement", same Abstract).
+//                       engine_only = 0: one 2-D copy per param over the
+//                       ranks whose shard is full plus a 1-D copy for the
+//                       partial rank, which the runtime executes with a
+//                       blit kernel on the compute units.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstring>
+#include <vector>
 
 #include "plan_format.h"
 #include "tide.h"
@@ -161,7 +167,6 @@ extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_onl
     const uint8_t* b = static_cast<const uint8_t*>(h_plan);
     const ParamDesc* ps = reinterpret_cast<const ParamDesc*>(b + h.off_params);
     const uint64_t* full = reinterpret_cast<const uint64_t*>(b + h.off_full);
-    const hipMemcpyKind kind = engine_only ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const char* g = reinterpret_cast<const char*>(h.gathered);
     for (int32_t p = 0; p < h.P; ++p) {
@@ -169,16 +174,30 @@ extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_onl
         std::memcpy(&d, ps + p, sizeof d);
         if (d.n == 0) continue;
         char* dst = reinterpret_cast<char*>(full[p]);
-        const int64_t nfull = d.d0 / d.s;  // ranks whose shard has s valid rows
+        const int64_t nfull = d.d0 / d.s;        // ranks whose shard has s valid rows
+        const int64_t rest = d.n - nfull * d.m;  // elements of the one partial rank
+        if (engine_only) {
+            // One 1-D copy per (param, rank) run: the runtime's no-compute-
+            // unit copy kind puts these on the DMA engines (a 2-D copy of
+            // the same kind is executed by a blit kernel).
+            const int64_t nruns = nfull + (rest > 0 ? 1 : 0);
+            for (int64_t r = 0; r < nruns && r < h.R; ++r) {
+                const int64_t cnt = r < nfull ? d.m : rest;
+                hipError_t e = hipMemcpyAsync(dst + 2 * r * d.m, g + 2 * (r * h.S + d.off),
+                                              (size_t)(2 * cnt), hipMemcpyDeviceToDeviceNoCU, s);
+                if (e != hipSuccess) return TIDE_EHIP;
+            }
+            continue;
+        }
         if (nfull > 0) {
             hipError_t e = hipMemcpy2DAsync(dst, (size_t)(2 * d.m), g + 2 * d.off, (size_t)(2 * h.S),
-                                            (size_t)(2 * d.m), (size_t)nfull, kind, s);
+                                            (size_t)(2 * d.m), (size_t)nfull,
+                                            hipMemcpyDeviceToDevice, s);
             if (e != hipSuccess) return TIDE_EHIP;
         }
-        const int64_t rest = d.n - nfull * d.m;  // rows of the one partial rank
         if (rest > 0 && nfull < h.R) {
             hipError_t e = hipMemcpyAsync(dst + 2 * nfull * d.m, g + 2 * (nfull * h.S + d.off),
-                                          (size_t)(2 * rest), kind, s);
+                                          (size_t)(2 * rest), hipMemcpyDeviceToDevice, s);
             if (e != hipSuccess) return TIDE_EHIP;
         }
     }
@@ -206,4 +225,47 @@ extern "C" tide_status tide_stream_create_cu_limited(int32_t n_cu, tide_stream_t
 extern "C" tide_status tide_stream_destroy(tide_stream_t stream) {
     if (!stream) return TIDE_EINVAL;
     return hipStreamDestroy(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? TIDE_OK : TIDE_EHIP;
+}
+
+extern "C" tide_status tide_ag_place_sdma_streams(const void* h_plan, const tide_stream_t* streams,
+                                                  int32_t n_streams) {
+    if (!h_plan || !streams || n_streams < 1 || n_streams > 64) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (!h.has_ag) return TIDE_EUNSUPPORTED;
+    const uint8_t* b = static_cast<const uint8_t*>(h_plan);
+    const ParamDesc* ps = reinterpret_cast<const ParamDesc*>(b + h.off_params);
+    const uint64_t* full = reinterpret_cast<const uint64_t*>(b + h.off_full);
+    const char* g = reinterpret_cast<const char*>(h.gathered);
+    struct Copy {
+        char* dst;
+        const char* src;
+        size_t bytes;
+    };
+    std::vector<Copy> copies;
+    for (int32_t p = 0; p < h.P; ++p) {
+        ParamDesc d;
+        std::memcpy(&d, ps + p, sizeof d);
+        if (d.n == 0) continue;
+        char* dst = reinterpret_cast<char*>(full[p]);
+        const int64_t nfull = d.d0 / d.s;
+        const int64_t rest = d.n - nfull * d.m;
+        const int64_t nruns = nfull + (rest > 0 ? 1 : 0);
+        for (int64_t r = 0; r < nruns && r < h.R; ++r) {
+            const int64_t cnt = r < nfull ? d.m : rest;
+            copies.push_back({dst + 2 * r * d.m, g + 2 * (r * h.S + d.off), (size_t)(2 * cnt)});
+        }
+    }
+    std::stable_sort(copies.begin(), copies.end(),
+                     [](const Copy& a, const Copy& c) { return a.bytes > c.bytes; });
+    std::vector<size_t> load((size_t)n_streams, 0);
+    for (const Copy& c : copies) {
+        size_t k = (size_t)(std::min_element(load.begin(), load.end()) - load.begin());
+        load[k] += c.bytes;
+        hipError_t e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDeviceNoCU,
+                                      reinterpret_cast<hipStream_t>(streams[k]));
+        if (e != hipSuccess) return TIDE_EHIP;
+    }
+    return TIDE_OK;
 }

@@ -58,7 +58,8 @@ def summarize_stats(d: str, out: str, command: str, top: int = 12) -> None:
         lines.append("# launch shapes (first dispatch of each kernel)")
         for k, t in list(seen.items())[:top]:
             lines.append("%-70s grid=%s wg=%s vgpr=%s sgpr=%s lds=%s scratch=%s" % (
-                k[:70], t.get("Grid_Size", "?"), t.get("Workgroup_Size", "?"),
+                k[:70], t.get("Grid_Size", t.get("Grid_Size_X", "?")),
+                t.get("Workgroup_Size", t.get("Workgroup_Size_X", "?")),
                 t.get("VGPR_Count", t.get("Arch_VGPR_Count", "?")), t.get("SGPR_Count", "?"),
                 t.get("LDS_Block_Size", t.get("Lds_Size", "?")),
                 t.get("Scratch_Size", "?")))

@@ -147,6 +147,22 @@ def test_random_bit_patterns_round_trip():
             assert torch.equal(full[p].cpu().view(torch.int16), t.view(torch.int16)), (engine, p)
 
 
+@pytest.mark.parametrize("n_streams", [1, 3, 8])
+def test_copy_engine_placement_over_streams(n_streams):
+    shapes = [(37, 16), (64, 64), (5,), (1001, 3), (8, 512)]
+    R = 4
+    w = _wl(shapes, R, key=340)
+    st = harness.setup(w, with_rs=False)
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    ev = torch.cuda.Event()
+    ev.record()
+    for s in streams:
+        s.wait_event(ev)
+    st.plan.ag_sdma_streams(streams)
+    torch.cuda.synchronize()
+    gu.check_ag_full(st)
+
+
 @pytest.mark.big
 @pytest.mark.parametrize("key", [2, 3, 4, 5])
 def test_full_size_placement(key):
