@@ -139,6 +139,7 @@ def main():
     ap.add_argument("--no-probe", action="store_true",
                     help="skip even the default-configuration GEMM probe")
     ap.add_argument("--no-sdma", action="store_true", help="skip timing the copy-engine placement")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a HIP graph")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of a plain device copy run once (counter calibration)")
     args = ap.parse_args()
@@ -208,6 +209,28 @@ def main():
     ag_gbs = agb / (ag_avg * 1e-3) / 1e9
     log("step %.3f ms; RS avg %.3f ms (min %.3f) = %.0f GB/s; AG avg %.3f ms = %.0f GB/s" % (
         ms_step, rs_avg, min(rs_ms), rs_gbs, ag_avg, ag_gbs))
+
+    # the same step captured once in a HIP graph and replayed (launch-bound
+    # host work removed; the device work is identical)
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ge0.record()
+        for _ in range(args.steps):
+            g.replay()
+        ge1.record()
+        torch.cuda.synchronize()
+        graph_ms = ge0.elapsed_time(ge1) / args.steps
+        log("step as a HIP graph: %.3f ms" % graph_ms)
+        del g
 
     sdma = None
     if not args.no_sdma:
@@ -283,6 +306,7 @@ def main():
         "ag_frac_hbm": round(ag_gbs / HBM_PEAK_GBS, 4),
         "ag_ms": round(ag_avg, 4),
         "ag_sdma": sdma,
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
         "rs_launches": n_launch,
         "rs_cus": rs_cus,

@@ -187,6 +187,38 @@ def test_launch_size_same_bits(launch_mib):
     gu.check_ag_full(st)
 
 
+def test_hip_graph_replays_match_eager():
+    """One step (placement + reduce-scatter, several launches each) captured
+    in a HIP graph: every replay, with eager work and synchronisation in
+    between, gives the eager bits (the library records no memset and no
+    allocation)."""
+    w = _wl([(1001, 96), (5,), (640, 64)], 8, key=167)
+    st = harness.setup(w, rs_tile=2048, ag_tile=2048, launch_mib=1)
+    st.plan.ag()
+    st.plan.rs()
+    torch.cuda.synchronize()
+    want_rs = [o.clone() for o in st.out]
+    want_ag = st.full_arena.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st.plan.ag()
+        st.plan.rs()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in st.out:
+            o.view(torch.int32).fill_(-1)
+        st.full_arena.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(want_rs, st.out):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+        assert torch.equal(want_ag.view(torch.int16), st.full_arena.view(torch.int16)), rep
+    gu.check_rs_full(st)
+
+
 def test_deterministic_repeat():
     w = _wl([(4096, 256), (7,)], 16, key=170, sigma=1e-3)
     st = harness.setup(w, with_ag=False)
