@@ -145,8 +145,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(all R simulated ranks live in one GPU's HBM); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library keeps all R simulated ranks in one "
+              "GPU's HBM and has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
