@@ -91,6 +91,42 @@ def test_unaligned_gathered_buffer(gshift, engine):
     assert np.all(f[:16] == gu.SENT16) and np.all(f[16 + n:] == gu.SENT16)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_fuzz_random_placements(seed):
+    """Seeded random problems and gathered-buffer offsets, both engines,
+    compared with the oracle bit for bit."""
+    rng = np.random.default_rng(2000 + seed)
+    R = int(rng.choice([1, 2, 3, 5, 8, 16, 33, 64]))
+    P = int(rng.integers(1, 7))
+    shapes = []
+    for _ in range(P):
+        nd = int(rng.integers(0, 4))
+        dims = [int(rng.integers(0, 300))] + [int(rng.integers(1, 40)) for _ in range(max(0, nd - 1))]
+        shapes.append(tuple(dims[:nd]))
+    align = int(rng.choice([1, 2, 8]))
+    gshift = int(rng.integers(0, 8))
+    tile = int(rng.choice([0, 2048]))
+    _, _, _, S = api.tide_desc_geometry(shapes, R, align)
+    big = torch.empty(R * S + 16, dtype=torch.bfloat16, device="cuda")
+    synth.bits_(big, 600 + seed)
+    gathered = big[gshift:gshift + R * S]
+    n = synth.arena_numel(shapes)
+    fa = torch.empty(n + 32, dtype=torch.bfloat16, device="cuda")
+    full = synth.views(fa[16:16 + n], shapes)
+    gu.say("fuzz ag", seed, R, shapes, align, gshift, tile)
+    want = [np.full(gu.numel(s), gu.SENT16, np.uint16) for s in shapes]
+    oracle.ag(shapes, R, gu.bits16(gathered), align=align, out=want)
+    for engine in ("cu", "sdma"):
+        fa.view(torch.int16).fill_(-1)
+        plan = api.Plan(shapes, R, gathered=gathered, full=full, align=align, ag_tile=tile)
+        plan.ag() if engine == "cu" else plan.ag_sdma()
+        torch.cuda.synchronize()
+        for p in range(len(shapes)):
+            gu.assert_bits_equal(gu.bits16(full[p]), want[p], "%s full[%d]" % (engine, p))
+        f = gu.bits16(fa)
+        assert np.all(f[:16] == gu.SENT16) and np.all(f[16 + n:] == gu.SENT16)
+
+
 def test_placement_of_rs_output_is_full_fold():
     """AG(bf16(RS shards)) equals bf16 of the full fold, all on the device."""
     shapes = [(1001, 24), (5,), (64, 64)]

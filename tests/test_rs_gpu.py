@@ -82,6 +82,35 @@ def test_tree_order_odd_rank_counts(R):
     gu.check_rs_full(st, "tree")
 
 
+def _random_problem(seed):
+    rng = np.random.default_rng(1000 + seed)
+    R = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 23, 32, 64, 70]))
+    P = int(rng.integers(1, 7))
+    shapes = []
+    for _ in range(P):
+        nd = int(rng.integers(0, 4))
+        dims = [int(rng.integers(0, 200))] + [int(rng.integers(1, 40)) for _ in range(max(0, nd - 1))]
+        shapes.append(tuple(dims[:nd]))
+    align = int(rng.choice([1, 1, 2, 4, 8]))
+    tile = int(rng.choice([0, 2048, 4096]))
+    launch = int(rng.choice([0, -1, 1]))
+    order = str(rng.choice(["fixed", "tree"]))
+    return R, shapes, align, tile, launch, order
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fuzz_random_problems(seed):
+    """Seeded random problems (rank counts 1-70, 0-d/empty/ragged shapes,
+    offset alignment, tile and launch sizes, both orders), compared with the
+    oracle over whole arenas, gaps and guard bands included."""
+    R, shapes, align, tile, launch, order = _random_problem(seed)
+    gu.say("fuzz", seed, R, shapes, align, tile, launch, order)
+    w = _wl(shapes, R, key=200 + seed)
+    st = harness.setup(w, with_ag=False, align=align, rs_tile=tile, launch_mib=launch)
+    _run(st, order)
+    gu.check_rs_full(st, order)
+
+
 @pytest.mark.parametrize("align", [4, 8, 64])
 def test_aligned_offsets_leave_gaps(align):
     w = _wl([(37, 16), (5,), (3, 3), (40, 8)], 4, key=131)
