@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,11 +39,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (a comment edit does not
+    change the kernel)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def src_hash(paths) -> str:
+    """Hash of the kernel sources' code (comments ignored), recorded in the
+    counter summaries so that stale counters are never reported."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(HERE, p), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, p)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -58,7 +69,7 @@ def read_traffic(kernel: str, workload: str, sources) -> dict:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_src_sha256_16") != src_hash(sources):
+    if kv.get("kernel_code_sha256_16 (comments stripped)") != src_hash(sources):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))

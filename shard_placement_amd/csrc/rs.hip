@@ -10,14 +10,18 @@
 //
 // Work decomposition: the host plan cuts every (param, rank) shard into
 // tiles (plan.cpp); one short-lived 256-lane workgroup takes one tile (or
-// strides over tiles when the grid is capped).  In a vector tile each lane
+// strides over tiles when the grid is capped), runs of 8 consecutive tiles
+// going to one XCD.  A call is cut into launches of about 256 MiB of
+// traffic (the plan's launch size) so that kernels on other queues get
+// whole compute units at the launch boundaries.  In a vector tile each lane
 // owns 8 consecutive elements: it issues one 16-byte load per rank (a batch
-// of ranks in flight at once), widens bf16 -> fp32 exactly (bits << 16),
-// adds in rank order 0..R-1 starting from rank 0's value, and writes
-// 2 x 16 bytes of fp32.  Padding tiles only write +0.0f.  Every access of a
-// wave is one contiguous 1 KB (loads) / 2 KB (stores) run: fully coalesced.
-// There is no LDS and no inter-workgroup communication.  The path is
-// HBM-bound (about 0.25-0.5 flop per byte), so there is no MFMA here.
+// of 8 ranks in flight at once), widens bf16 -> fp32 exactly (bits << 16),
+// adds in rank order 0..R-1 starting from rank 0's value (or pairwise, tree
+// order), and hands its 8 results through the wave's own 2 KB of LDS so
+// that each of the wave's two 16-byte-per-lane stores covers one
+// contiguous 1 KB run.  Padding tiles only write +0.0f.  There is no
+// inter-workgroup communication.  The path is HBM-bound (about 0.25-0.5
+// flop per byte), so there is no MFMA here.
 #include <hip/hip_runtime.h>
 
 #include <climits>

@@ -101,7 +101,7 @@ def summarize_pmc(fetch_dir, write_dir, out, kernel, calib_kernel, calib_bytes,
         "command_write: %s" % command_write,
         "kernel: %s" % kernel,
         "workload: %s" % workload,
-        "kernel_src_sha256_16: %s" % src_hash,
+        "kernel_code_sha256_16 (comments stripped): %s" % src_hash,
         "dispatches_fetch: %d" % len(f),
         "dispatches_write: %d" % len(w),
         "fetch_kib_median: %.1f" % (fetch / kib),
