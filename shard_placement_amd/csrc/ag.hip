@@ -121,6 +121,56 @@ __device__ __forceinline__ void copy_scalar(const uint16_t* __restrict__ src,
     for (int e = threadIdx.x; e < len; e += kBlock) d[e] = s[e];
 }
 
+// Realigning copy: the destination is 16-byte aligned, the source sits
+// `shift` bytes (2..14, even) past a 16-byte boundary.  Lane c reads the two
+// aligned 16-byte source blocks that cover its 16 output bytes and funnels
+// them into place with byte-align operations, so both loads and stores are
+// 16-byte and every wave instruction covers one contiguous 1 KB run (the
+// second block is the next lane's first: an L2 hit).  The plan leaves at
+// least 8 elements of the run on both sides of such a tile, so the aligned
+// blocks (up to 16 bytes beyond the tile's own bytes) stay in the run.
+template <bool NTL, bool NTS>
+__device__ __forceinline__ void copy_shift(const uint16_t* __restrict__ src,
+                                           uint16_t* __restrict__ dst, int len) {
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(src);
+    const int shift = (int)(sa & 15);
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(sa - (uintptr_t)shift);
+    const int q = shift >> 2, r = (shift & 3) * 8;
+    constexpr int kStep = kBlock * kVec;
+    for (int e0 = 0; e0 < len; e0 += kStep * 2) {
+        u32x4 lo[2], hi[2];
+        bool ok[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = e0 + u * kStep + threadIdx.x * kVec;
+            ok[u] = e < len;
+            const int ec = ok[u] ? e : 0;
+            lo[u] = ld16<NTL>(base + ec);
+            hi[u] = ld16<NTL>(base + ec + kVec);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t w[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w,
+                                   hi[u].x, hi[u].y, hi[u].z, hi[u].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // bytes [shift + 4k, shift + 4k + 4) of the 32-byte window
+                uint32_t a = 0, b = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (t == q) {
+                        a = w[t + k];
+                        b = w[t + k + 1];
+                    }
+                o[k] = r ? ((a >> r) | (b << (32 - r))) : a;
+            }
+            const int e = e0 + u * kStep + threadIdx.x * kVec;
+            if (ok[u]) st16<NTS>(dst + e, u32x4{o[0], o[1], o[2], o[3]});
+        }
+    }
+}
+
 template <bool NTL, bool NTS>
 __global__ __launch_bounds__(kBlock) void ag_kernel(const AgTile* __restrict__ tiles,
                                                     int64_t ntiles,
@@ -134,6 +184,8 @@ __global__ __launch_bounds__(kBlock) void ag_kernel(const AgTile* __restrict__ t
             copy_vec16<NTL, NTS>(src, dst, tile.len);
         else if (tile.kind == kAgVec4)
             copy_vec4(src, dst, tile.len);
+        else if (tile.kind == kAgShift)
+            copy_shift<NTL, NTS>(src, dst, tile.len);
         else
             copy_scalar(src, dst, tile.len);
     }

@@ -169,6 +169,7 @@ def test_ag_tiles_cover_valid_rows_only(R, gmis):
     blob, info = api.tide_desc_build(SHAPES, R, None, None, ga + gmis, f, ag_tile=2048)
     h, ps, _, _, ag = decode(blob)
     assert h["has_rs"] == 0 and h["has_ag"] == 1 and info.rs_tiles == 0
+    shifted = 0
     for p, d in enumerate(ps):
         tiles = sorted((int(t["dst"]), int(t["src"]), int(t["len"]), int(t["kind"]))
                        for t in ag if t["p"] == p)
@@ -184,6 +185,14 @@ def test_ag_tiles_cover_valid_rows_only(R, gmis):
             # never crosses into the rank's padding rows
             valid = min(max(int(d["d0"]) - r * int(d["s"]), 0), int(d["s"])) * int(d["c"])
             assert dst + ln <= r * int(d["m"]) + valid
+            if kind == 3:
+                # realigning copy: aligned destination, 8 elements of the same
+                # run on both sides (its aligned source blocks stay in the run)
+                assert (f[p] + 2 * dst) % 16 == 0 and ln % 8 == 0
+                assert (ga + gmis + 2 * src) % 16 != 0
+                run0 = r * int(d["m"])
+                assert dst - 8 >= run0 and dst + ln + 8 <= run0 + valid
+                shifted += 1
             pos = dst + ln
         assert pos == int(d["n"])
 
@@ -287,3 +296,20 @@ def test_launch_granularity():
     _, small = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=1)
     assert small.rs_launch_tiles == max(1, (1 << 20) // per_tile)
     assert _status(api.tide_desc_build, shapes, R, g, o, ga, f, 1, 0, 0, -1, -2) == -1
+
+
+@pytest.mark.parametrize("gmis", [2, 4, 6, 10, 14])
+def test_ag_realigning_tiles_for_shifted_slots(gmis):
+    """Slots 16-byte-misaligned against aligned full tensors get realigning
+    tiles with 8 elements of the run on each side."""
+    shapes = [(4096, 8)]
+    R = 2
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    _, _, ga, f = _fake_ptrs(shapes, R, S)
+    blob, _ = api.tide_desc_build(shapes, R, None, None, ga + gmis, f)
+    _, ps, _, _, ag = decode(blob)
+    kinds = ag["kind"].tolist()
+    assert 3 in kinds
+    for t in ag:
+        if t["kind"] != 3:
+            assert t["len"] < 64
