@@ -89,7 +89,7 @@ typedef struct tide_shape {
 typedef struct tide_opts {
     int64_t align_elems;   /* arena/slot offset alignment, elements (>= 1; default 1) */
     int32_t rs_tile_elems; /* elements per reduce-scatter tile, multiple of 2048
-                              (0: chosen from R, about 128 KB of traffic) */
+                              (0: chosen from R, about 64 KB of traffic) */
     int32_t ag_tile_elems; /* elements per placement tile, multiple of 2048 (0: 2048) */
     int32_t flags;         /* -1: library default (both hints); else an OR of TIDE_FLAG_* */
     int32_t launch_mib;    /* algorithmic MiB moved per kernel launch: a call is cut

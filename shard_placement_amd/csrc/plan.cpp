@@ -25,12 +25,13 @@ constexpr int64_t kSection = 256;
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-// Default reduce-scatter tile: at most about 128 KB of HBM traffic per tile
-// (R*2 + 4 bytes per element), a power of two in [2048, 32768] elements.
-// Short tiles measured fastest on MI355X (many short-lived workgroups keep
-// more independent loads in flight than long-running ones).
+// Default reduce-scatter tile: at most about 64 KB of HBM traffic per tile
+// (R*2 + 4 bytes per element), a power of two in [2048, 32768] elements, so
+// 2048 elements (one pass of a 256-lane workgroup) from R = 8 up.  Short
+// tiles measured fastest on MI355X (R = 8: 2048 -> 5.90, 4096 -> 5.75,
+// 8192 -> 5.48 TB/s with 256 MiB launches).
 int32_t default_rs_tile(int32_t R) {
-    int64_t want = (int64_t)131072 / (2 * (int64_t)R + 4);
+    int64_t want = (int64_t)65536 / (2 * (int64_t)R + 4);
     int64_t t = kTileQuantum;
     while (t * 2 <= want && t < 32768) t *= 2;
     return (int32_t)t;

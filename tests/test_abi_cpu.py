@@ -146,7 +146,7 @@ def test_rs_vector_tiles_dominate_when_aligned():
     blob, info = api.tide_desc_build(shapes, R, g, o)
     _, _, _, rs, _ = decode(blob)
     assert set(rs["kind"].tolist()) == {0}
-    assert info.rs_tile_elems == 4096
+    assert info.rs_tile_elems == 2048
     assert int(rs["len"].sum()) == R * S
 
 
