@@ -259,6 +259,19 @@ def main():
                 "engine": "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run"}
         log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
 
+    # which compute units the reduce-scatter ran on (one census call, outside
+    # the timed region: same launches, each tile records its CU's hardware id)
+    census = st.plan.rs_census(max_workgroups=args.max_wg)
+    torch.cuda.synchronize()
+    ids = census.cpu().tolist()
+    cus_measured = len(set(ids))
+    per_xcc = {}
+    for v in set(ids):
+        per_xcc[v >> 8] = per_xcc.get(v >> 8, 0) + 1
+    log("census: %d distinct CUs over %d tiles; per XCC %s" % (cus_measured, len(ids),
+                                                              dict(sorted(per_xcc.items()))))
+    del census
+
     probe = None
     if not args.no_probe:
         from shard_placement_amd import probe as probe_mod
@@ -291,9 +304,6 @@ def main():
         log("cpu baseline", cpu)
 
     n_launch = -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles)))
-    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
-    grid = int(info.rs_launch_tiles) if args.max_wg == 0 else min(args.max_wg, int(info.rs_launch_tiles))
-    rs_cus = min(grid, n_cus)  # workgroups spread over every CU when the grid exceeds them
     rec = {
         "metric": "RS bf16->fp32 shard GB/s & % of HBM peak; AG placement GB/s; GEMM slowdown %",
         "value": round((rsb + agb) / (ms_step * 1e-3) / 1e9, 1),
@@ -320,8 +330,9 @@ def main():
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
         "rs_launches": n_launch,
-        "rs_cus": rs_cus,
-        "rs_cu_ms": round(rs_cus * rs_avg, 1),
+        "rs_cus": cus_measured,
+        "rs_cus_per_xcc": {str(k): v for k, v in sorted(per_xcc.items())},
+        "rs_cu_ms": round(cus_measured * rs_avg, 1),
         "probe": probe,
         # per kernel launch: one reduce-scatter call is n_launch launches of
         # about rsb / n_launch algorithmic bytes; the event time per call

@@ -184,6 +184,18 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
                                        int64_t tile_count, int32_t max_workgroups,
                                        tide_stream_t stream);
 
+/* The reduce-scatter of tide_rs_bf16_to_fp32 (same launches, same
+ * results) that also records, for every tile t of the plan, the compute
+ * unit that processed it: census[t] = xcc_id << 8 | se_id << 5 | sh_id << 4
+ * | cu_id (the GPU's hardware-ID registers).  census: device memory of at
+ * least census_len >= rs_tiles uint32 words.  Counting the distinct values
+ * gives the number of compute units the reduce-scatter occupied (the one-GPU
+ * analog of the pages' reduce-scatter "SM time" [Abstract]). */
+tide_status tide_rs_bf16_to_fp32_census(const void *h_plan, const void *d_plan,
+                                        int32_t order, int32_t max_workgroups,
+                                        uint32_t *census, int64_t census_len,
+                                        tide_stream_t stream);
+
 /* All-gather placement on the compute units [Abstract: TIDE-AG]: for
  * every param p and rank r, the clamp(d0 - r*s, 0, s) valid rows of slot r
  * are copied to rows [r*s, ...) of full[p]; slot padding is never read.

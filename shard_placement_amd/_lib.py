@@ -22,7 +22,8 @@ FLAG_NT_STORES = 2
 EXPORTS = ("tide_abi_version", "tide_status_str", "tide_desc_size", "tide_desc_geometry",
            "tide_desc_build", "tide_plan_query", "tide_rs_bf16_to_fp32", "tide_ag_place",
            "tide_ag_place_sdma", "tide_stream_create_cu_limited", "tide_stream_destroy",
-           "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams")
+           "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams",
+           "tide_rs_bf16_to_fp32_census")
 
 
 class TideShape(ctypes.Structure):
@@ -94,10 +95,12 @@ def lib():
     L.tide_stream_create_cu_limited.argtypes = [i32, ctypes.POINTER(vp)]
     L.tide_stream_destroy.argtypes = [vp]
     L.tide_ag_place_sdma_streams.argtypes = [vp, ctypes.POINTER(vp), i32]
+    L.tide_rs_bf16_to_fp32_census.argtypes = [vp, vp, i32, i32, vp, i64, vp]
     for name in ("tide_desc_size", "tide_desc_geometry", "tide_desc_build", "tide_plan_query",
                  "tide_rs_bf16_to_fp32", "tide_ag_place", "tide_ag_place_sdma",
                  "tide_stream_create_cu_limited", "tide_stream_destroy",
-                 "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams"):
+                 "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams",
+                 "tide_rs_bf16_to_fp32_census"):
         getattr(L, name).restype = ctypes.c_int
     if L.tide_abi_version() != 1:
         raise RuntimeError("libtide ABI version %d, expected 1" % L.tide_abi_version())

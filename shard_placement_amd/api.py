@@ -120,6 +120,16 @@ def tide_rs_bf16_to_fp32_tiles(h_plan: np.ndarray, d_plan: torch.Tensor, order: 
           "tide_rs_bf16_to_fp32_tiles")
 
 
+def tide_rs_bf16_to_fp32_census(h_plan: np.ndarray, d_plan: torch.Tensor, census: torch.Tensor,
+                                order: int = 0, max_workgroups: int = 0, stream=None) -> None:
+    if census.dtype != torch.int32 or census.device.type != "cuda" or not census.is_contiguous():
+        raise TideError(-6, "census must be a contiguous int32 GPU tensor")
+    check(_lib.lib().tide_rs_bf16_to_fp32_census(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
+                                                 int(max_workgroups), census.data_ptr(),
+                                                 census.numel(), _stream(stream)),
+          "tide_rs_bf16_to_fp32_census")
+
+
 def tide_ag_place(h_plan: np.ndarray, d_plan: torch.Tensor, max_workgroups: int = 0,
                   stream=None) -> None:
     check(_lib.lib().tide_ag_place(h_plan.ctypes.data, d_plan.data_ptr(), int(max_workgroups),
@@ -243,6 +253,15 @@ class Plan:
                                        min(chunk_tiles, n - b), max_workgroups, stream)
             launches += 1
         return launches
+
+    def rs_census(self, order: str = "fixed", max_workgroups: int = 0, stream=None) -> torch.Tensor:
+        """The reduce-scatter, returning for every tile the packed id of the
+        compute unit that processed it (int32 GPU tensor)."""
+        census = torch.full((max(1, int(self.info.rs_tiles)),), -1, dtype=torch.int32,
+                            device=self.d_blob.device)
+        tide_rs_bf16_to_fp32_census(self.blob, self.d_blob, census, ORDERS[order],
+                                    max_workgroups, stream)
+        return census
 
     def ag(self, max_workgroups: int = 0, stream=None) -> None:
         tide_ag_place(self.blob, self.d_blob, max_workgroups, stream)

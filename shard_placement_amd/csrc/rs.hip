@@ -106,6 +106,16 @@ __device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles) {
     return (i / kXcdGroup) * span + x * kXcdGroup + (i % kXcdGroup);
 }
 
+// The compute unit a workgroup runs on, for the optional census: the HW_ID
+// hardware register's cu_id [11:8], sh_id [12] and se_id [15:13] fields
+// and the XCC_ID register's xcc_id [3:0], packed as xcc << 8 | (HW_ID >> 8
+// & 0xff).  Reading the registers has no side effect.
+__device__ __forceinline__ uint32_t hw_cu_id() {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);    // HW_ID
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20);  // XCC_ID
+    return ((xcc & 0xfu) << 8) | ((hw >> 8) & 0xffu);
+}
+
 __device__ __forceinline__ const uint16_t* src_of(const uint64_t* gp, int q) {
     return reinterpret_cast<const uint16_t*>(gp[q]);
 }
@@ -360,11 +370,13 @@ __global__ __launch_bounds__(kBlock) void rs_tree_kernel(const RsTile* __restric
                                                          int64_t ntiles,
                                                          const uint64_t* __restrict__ gptr,
                                                          const uint64_t* __restrict__ obase,
-                                                         int R) {
+                                                         int R, uint32_t* __restrict__ census) {
     __shared__ float lds[kBlock * kVec];
     float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
     for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
-        const RsTile tile = tiles[tile_of(b, ntiles)];
+        const int64_t t = tile_of(b, ntiles);
+        if (census && threadIdx.x == 0) census[t] = hw_cu_id();
+        const RsTile tile = tiles[t];
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
         const uint64_t* gp = gptr + (int64_t)tile.p * R;
         if (tile.kind == kRsVec)
@@ -381,11 +393,13 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
                                                           int64_t ntiles,
                                                           const uint64_t* __restrict__ gptr,
                                                           const uint64_t* __restrict__ obase,
-                                                          int R) {
+                                                          int R, uint32_t* __restrict__ census) {
     __shared__ float lds[kBlock * kVec];
     float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
     for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
-        const RsTile tile = tiles[tile_of(b, ntiles)];
+        const int64_t t = tile_of(b, ntiles);
+        if (census && threadIdx.x == 0) census[t] = hw_cu_id();
+        const RsTile tile = tiles[t];
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
         const uint64_t* gp = gptr + (int64_t)tile.p * R;
         if (tile.kind == kRsVec)
@@ -397,7 +411,7 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
     }
 }
 
-typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int);
+typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int, uint32_t*);
 
 template <int RB, bool EXACT, int U>
 RsKernel pick_nt(uint32_t flags) {
@@ -446,7 +460,8 @@ RsKernel pick_tree(int R, uint32_t flags) {
 namespace {
 
 tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int64_t tile_begin,
-                      int64_t tile_count, int32_t max_workgroups, tide_stream_t stream) {
+                      int64_t tile_count, int32_t max_workgroups, tide_stream_t stream,
+                      uint32_t* census = nullptr, int64_t census_len = 0) {
     if (!h_plan || !d_plan) return TIDE_EINVAL;
     PlanHeader h;
     std::memcpy(&h, h_plan, sizeof h);
@@ -460,6 +475,7 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         tile_count > h.n_rs_tiles - tile_begin)
         return TIDE_EINVAL;
     if (tile_count == 0) return TIDE_OK;
+    if (census && census_len < tile_count) return TIDE_EINVAL;
 
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
     const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
@@ -478,7 +494,8 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         int64_t grid = ntiles;
         if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
         if (grid > INT_MAX) grid = INT_MAX;
-        void* args[] = {&tiles, &ntiles, &gptr, &obase, &R};
+        uint32_t* cen = census ? census + (b - tile_begin) : nullptr;
+        void* args[] = {&tiles, &ntiles, &gptr, &obase, &R, &cen};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
                                        dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return TIDE_EHIP;
@@ -499,4 +516,12 @@ extern "C" tide_status tide_rs_bf16_to_fp32_tiles(const void* h_plan, const void
                                                   tide_stream_t stream) {
     if (tile_count < 0) return TIDE_EINVAL;
     return launch_rs(h_plan, d_plan, order, tile_begin, tile_count, max_workgroups, stream);
+}
+
+extern "C" tide_status tide_rs_bf16_to_fp32_census(const void* h_plan, const void* d_plan,
+                                                   int32_t order, int32_t max_workgroups,
+                                                   uint32_t* census, int64_t census_len,
+                                                   tide_stream_t stream) {
+    if (!census) return TIDE_EINVAL;
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream, census, census_len);
 }

@@ -248,6 +248,33 @@ def test_hip_graph_replays_match_eager():
     gu.check_rs_full(st)
 
 
+def test_cu_census_same_bits_and_counts():
+    """The census call gives the same shards and names a compute unit for
+    every tile; confined to a CU-masked stream it names at most that many."""
+    w = _wl([(4096, 256), (7,)], 8, key=168, sigma=1e-3)
+    st = harness.setup(w, with_ag=False)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    census = st.plan.rs_census()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, st.out):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    c = census.cpu()
+    assert int((c < 0).sum()) == 0
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 1 <= len(set(c.tolist())) <= ncu
+    s = api.tide_stream_create_cu_limited(8)
+    try:
+        c8 = st.plan.rs_census(stream=s)
+        torch.cuda.synchronize()
+        assert 1 <= len(set(c8.cpu().tolist())) <= 8
+    finally:
+        api.tide_stream_destroy(s)
+
+
 def test_deterministic_repeat():
     w = _wl([(4096, 256), (7,)], 16, key=170, sigma=1e-3)
     st = harness.setup(w, with_ag=False)
