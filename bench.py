@@ -25,6 +25,7 @@ import os
 import re
 import sys
 import time
+from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
@@ -57,9 +58,10 @@ def src_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str, sources) -> dict:
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+def read_traffic(kernel: str, workload: str, sources) -> Optional[float]:
+    """HBM bytes over algorithmic bytes for one launch, from a committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
     path = os.path.join(PROFILES, "%s_%s_pmc.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -72,8 +74,8 @@ def read_traffic(kernel: str, workload: str, sources) -> dict:
     if kv.get("kernel_code_sha256_16 (comments stripped)") != src_hash(sources):
         return None
     try:
-        return int(float(kv["hbm_bytes_per_launch"]))
-    except (KeyError, ValueError):
+        return float(kv["hbm_bytes_per_launch"]) / float(kv["algorithmic_bytes_per_launch"])
+    except (KeyError, ValueError, ZeroDivisionError):
         return None
 
 
@@ -143,6 +145,8 @@ def main():
     ap.add_argument("--launch-mib", type=int, default=0, help="MiB per kernel launch (0: default, -1: one launch)")
     ap.add_argument("--ag-tile", type=int, default=0)
     ap.add_argument("--max-wg", type=int, default=0, help="cap the RS grid (0: one workgroup per tile)")
+    ap.add_argument("--rank-layout", choices=("packed", "separate"), default="packed",
+                    help="simulated ranks' arenas as rows of one allocation, or one allocation each")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
@@ -171,7 +175,7 @@ def main():
     log("workload", w.name, "R", w.R, "P", w.P, "N", w.numel())
     t0 = time.perf_counter()
     st = harness.setup(w, guard=0, flags=args.flags, rs_tile=args.rs_tile, ag_tile=args.ag_tile,
-                       launch_mib=args.launch_mib)
+                       launch_mib=args.launch_mib, rank_layout=args.rank_layout)
     torch.cuda.synchronize()
     info = st.plan.info
     log("setup %.1f s; plan: %d RS tiles of %d (%d per launch), %d AG tiles of %d (%d per launch), "
@@ -296,7 +300,7 @@ def main():
         for m in probe["modes"]:
             log("probe", m)
 
-    traffic = read_traffic("rs_fixed_kernel", w.name, RS_SOURCES)
+    traffic_ratio = read_traffic("rs_fixed_kernel", w.name, RS_SOURCES)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host cores")
@@ -304,6 +308,9 @@ def main():
         log("cpu baseline", cpu)
 
     n_launch = -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles)))
+    algo_launch = rsb // n_launch
+    # counters were read on full launches; scaled here to the average launch
+    traffic = round(traffic_ratio * algo_launch) if traffic_ratio else None
     rec = {
         "metric": "RS bf16->fp32 shard GB/s & % of HBM peak; AG placement GB/s; GEMM slowdown %",
         "value": round((rsb + agb) / (ms_step * 1e-3) / 1e9, 1),
@@ -319,6 +326,7 @@ def main():
         "data": "synthetic: seeded bf16 N(0,%g) gradients shaped like %s" % (w.sigma, w.name),
         "config": {"workload": w.name, "R": w.R, "P": w.P, "N": w.numel(),
                    "step": "AG placement + fused RS", "slot_reuse": w.slot_reuse,
+                   "rank_layout": args.rank_layout,
                    "rs_bytes": rsb, "ag_bytes": agb},
         "rs_gbps": round(rs_gbs, 1),
         "rs_frac_hbm": round(rs_gbs / HBM_PEAK_GBS, 4),
@@ -341,7 +349,8 @@ def main():
                      "unit": "GB/s", "frac": round(rs_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "rs_fixed_kernel",
                      "launches_per_call": n_launch,
-                     "algorithmic_bytes_per_launch": rsb // n_launch,
+                     "algorithmic_bytes_per_launch": algo_launch,
+                     "traffic_over_algorithmic": round(traffic_ratio, 4) if traffic_ratio else None,
                      "avg_launch_ms": round(rs_avg / n_launch, 5),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, "
                                      "copy-calibrated)"},

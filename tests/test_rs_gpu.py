@@ -71,6 +71,20 @@ def test_ragged_shapes_bitwise(R, shapes, tile, order):
     gu.check_rs_full(st, order)
 
 
+@pytest.mark.parametrize("R,shapes", RANDOM_CASES[::3], ids=[str(c[0]) for c in RANDOM_CASES[::3]])
+@pytest.mark.parametrize("slot_reuse", [False, True])
+def test_rank_arenas_allocated_separately(R, shapes, slot_reuse):
+    """Every rank's gradient and output arena in an allocation of its own
+    (the packed rows are the default): same bits."""
+    if slot_reuse and R < 2:
+        pytest.skip("Slot-Reuse needs R >= 2")
+    w = _wl(shapes, R, key=100 + R)
+    gu.say("separate arenas R", R, shapes, slot_reuse)
+    st = harness.setup(w, with_ag=False, rank_layout="separate", slot_reuse=slot_reuse)
+    _run(st)
+    gu.check_rs_full(st, "fixed")
+
+
 @pytest.mark.parametrize("R", [3, 5, 6, 7, 11, 13, 100, 129, 300])
 def test_tree_order_odd_rank_counts(R):
     """Tree order for rank counts that are not powers of two (odd elements
