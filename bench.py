@@ -79,6 +79,47 @@ def read_traffic(kernel: str, workload: str, sources) -> Optional[float]:
         return None
 
 
+def stock_leg(st, rsb: int, agb: int, reps: int = 3) -> dict:
+    """Time the one-GPU analog of stock FSDP2's layout conversion (pack the
+    ranks' gradients into a rank-major fp32 buffer, add in rank order, copy
+    the gathered buffer out into padded parameter buffers; torch operators)
+    on the same buffers, and check it gives the fused path's bits."""
+    import torch
+
+    from shard_placement_amd import stock
+
+    sp = stock.StockPath.from_setup(st)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    st.plan.ag()  # the gathered buffer may have changed since the last placement
+    ag_ms = timed(sp.ag)
+    same_ag = sp.same_ag_bits(st.full)
+    rs_ms = timed(sp.rs)
+    same_rs = sp.same_rs_bits(st.out)
+    pack_ms = timed(sp.pack)
+    traffic = stock.rs_traffic(st.w, st.S)
+    rec = {"ops": "torch._chunk_cat (cast+pack per rank) + add_ in rank order; "
+                  "torch.split_with_sizes_copy into padded parameter buffers",
+           "rs_ms": round(rs_ms, 4), "rs_effective_gbps": round(rsb / (rs_ms * 1e-3) / 1e9, 1),
+           "rs_hbm_bytes": traffic, "rs_hbm_gbps": round(traffic / (rs_ms * 1e-3) / 1e9, 1),
+           "pack_ms": round(pack_ms, 4),
+           "ag_ms": round(ag_ms, 4), "ag_effective_gbps": round(agb / (ag_ms * 1e-3) / 1e9, 1),
+           "same_bits_as_fused": bool(same_rs and same_ag)}
+    del sp
+    torch.cuda.empty_cache()
+    return rec
+
+
 def cpu_baseline(st, budget_s: float, max_passes: int = 3):
     """Time the CPU oracle (all host threads) on a bounded sample of the same
     workload: whole params in order until about budget_s of oracle time (the
@@ -155,6 +196,8 @@ def main():
                     help="skip even the default-configuration GEMM probe")
     ap.add_argument("--no-sdma", action="store_true", help="skip timing the copy-engine placement")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a HIP graph")
+    ap.add_argument("--no-stock", action="store_true",
+                    help="skip timing the stock-FSDP2 analog (pack, add, copy out in torch ops)")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of a plain device copy run once (counter calibration)")
     args = ap.parse_args()
@@ -276,6 +319,13 @@ def main():
                                                               dict(sorted(per_xcc.items()))))
     del census
 
+    stock_rec = None
+    if not args.no_stock:
+        stock_rec = stock_leg(st, rsb, agb)
+        stock_rec["fused_rs_speedup"] = round(stock_rec["rs_ms"] / rs_avg, 2)
+        stock_rec["fused_ag_speedup"] = round(stock_rec["ag_ms"] / ag_avg, 2)
+        log("stock-FSDP2 analog", stock_rec)
+
     probe = None
     if not args.no_probe:
         from shard_placement_amd import probe as probe_mod
@@ -341,6 +391,7 @@ def main():
         "rs_cus": cus_measured,
         "rs_cus_per_xcc": {str(k): v for k, v in sorted(per_xcc.items())},
         "rs_cu_ms": round(cus_measured * rs_avg, 1),
+        "stock_analog": stock_rec,
         "probe": probe,
         # per kernel launch: one reduce-scatter call is n_launch launches of
         # about rsb / n_launch algorithmic bytes; the event time per call
