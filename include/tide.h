@@ -221,6 +221,51 @@ tide_status tide_ag_place_sdma(const void *h_plan, int32_t engine_only,
 tide_status tide_ag_place_sdma_streams(const void *h_plan, const tide_stream_t *streams,
                                        int32_t n_streams);
 
+/* The same placement on the DMA copy engines, issued through ROCr: one 1-D
+ * copy per (param, rank) run, each pinned to one engine, spread over all
+ * the device's engines (largest first, each to the engine with the fewest
+ * bytes so far) [Abstract: no SMs used for transport or placement].
+ * Host-synchronous: waits for `stream` to finish its earlier work, then
+ * returns when every copy has completed (no kernel runs).  Do not overlap
+ * it with the runtime's own copy-engine copies (tide_ag_place_sdma, D2H
+ * copies) on the same device.  TIDE_EUNSUPPORTED: the device has no copy
+ * engine the runtime reports. */
+tide_status tide_ag_place_dma(const void *h_plan, tide_stream_t stream);
+
+/* Number of DMA copy engines tide_ag_place_dma / tide_rs_stage_dma use on
+ * the current device (*count = 0 and TIDE_EUNSUPPORTED if none). */
+tide_status tide_dma_engine_count(int32_t *count);
+
+/* Copy-engine-staged reduce-scatter [Abstract: copy engines and short-lived
+ * thread blocks; Design], in two calls.
+ *
+ * Staging buffers: h_stage[r] (host array of R device addresses) is rank
+ * r's staging buffer of R slots of bf16; slot q starts slot_stride elements
+ * after slot q-1 (slot_stride >= S) and is laid out like rank r's fp32
+ * arena (param p at element off[p], m_p elements).  A rank's vacated
+ * gathered buffer (R*S elements) is such a buffer with slot_stride = S.  The
+ * buffers must not overlap each other, any gradient tensor or any output
+ * arena (TIDE_EOVERLAP); they are 2-byte aligned (TIDE_EALIGN), and 16-byte
+ * aligned buffers with slot_stride % 8 == 0 let the fold use 16-byte loads.
+ *
+ * Phase 1, tide_rs_stage_dma: for every param p, output rank r and source
+ * rank q, the valid part of rank q's slice of p (flat indices [r*m_p,
+ * r*m_p + v*c), v = clamp(d0 - r*s, 0, s)) is copied by the DMA engines to
+ * slot q of h_stage[r] at element off[p]; padding rows are not copied.
+ * Host-synchronous like tide_ag_place_dma.
+ *
+ * Phase 2, tide_rs_fold_staged: a kernel folds each rank's R slots into its
+ * fp32 arena with the reduce-scatter's tiles, rank order and bits (padding
+ * rows +0.0, read from nowhere).  d_stage: a device copy of the R
+ * addresses (8-byte aligned).  Asynchronous on `stream`, cut into launches
+ * like tide_rs_bf16_to_fp32; order 0 fixed, 1 tree. */
+tide_status tide_rs_stage_dma(const void *h_plan, const uint64_t *h_stage,
+                              int64_t slot_stride, tide_stream_t stream);
+tide_status tide_rs_fold_staged(const void *h_plan, const void *d_plan, int32_t order,
+                                const uint64_t *h_stage, const uint64_t *d_stage,
+                                int64_t slot_stride, int32_t max_workgroups,
+                                tide_stream_t stream);
+
 /* A stream whose kernels may run only on the first n_cu compute units of
  * the device's CU mask (hipExtStreamCreateWithCUMask; default priority), for
  * confining the reduce-scatter's workgroups to part of the chip next to

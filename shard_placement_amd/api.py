@@ -147,6 +147,36 @@ def tide_ag_place_sdma_streams(h_plan: np.ndarray, streams) -> None:
           "tide_ag_place_sdma_streams")
 
 
+def tide_ag_place_dma(h_plan: np.ndarray, stream=None) -> None:
+    """Placement on the DMA engines (ROCr engine-pinned copies); returns
+    when the copies are done."""
+    check(_lib.lib().tide_ag_place_dma(h_plan.ctypes.data, _stream(stream)), "tide_ag_place_dma")
+
+
+def tide_dma_engine_count() -> int:
+    n = ctypes.c_int32(0)
+    check(_lib.lib().tide_dma_engine_count(ctypes.byref(n)), "tide_dma_engine_count")
+    return int(n.value)
+
+
+def tide_rs_stage_dma(h_plan: np.ndarray, h_stage: np.ndarray, slot_stride: int,
+                      stream=None) -> None:
+    """Phase 1 of the copy-engine-staged reduce-scatter; h_stage: uint64
+    array of R device addresses.  Returns when the copies are done."""
+    check(_lib.lib().tide_rs_stage_dma(h_plan.ctypes.data, h_stage.ctypes.data, int(slot_stride),
+                                       _stream(stream)), "tide_rs_stage_dma")
+
+
+def tide_rs_fold_staged(h_plan: np.ndarray, d_plan: torch.Tensor, order: int,
+                        h_stage: np.ndarray, d_stage: torch.Tensor, slot_stride: int,
+                        max_workgroups: int = 0, stream=None) -> None:
+    """Phase 2: fold the staged slots into the fp32 arenas (asynchronous)."""
+    check(_lib.lib().tide_rs_fold_staged(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
+                                         h_stage.ctypes.data, d_stage.data_ptr(),
+                                         int(slot_stride), int(max_workgroups), _stream(stream)),
+          "tide_rs_fold_staged")
+
+
 def tide_stream_create_cu_limited(n_cu: int) -> torch.cuda.ExternalStream:
     """A torch stream wrapping a HIP stream confined to the first n_cu CUs.
     Release it with tide_stream_destroy."""
@@ -274,9 +304,43 @@ class Plan:
         orders them against other work (e.g. with events)."""
         tide_ag_place_sdma_streams(self.blob, streams)
 
+    def ag_dma(self, stream=None) -> None:
+        """Placement on the DMA engines through ROCr (host-synchronous)."""
+        tide_ag_place_dma(self.blob, stream)
+
     def shard(self, out_arena: torch.Tensor, p: int) -> torch.Tensor:
         """View of param p's shard in one rank's fp32 arena, shaped [s, rest...]."""
         shp = self.shapes[p]
         s = int(self.m[p]) // (int(np.prod(shp[1:])) if len(shp) > 1 else 1) if int(self.m[p]) else 0
         v = out_arena[int(self.off[p]):int(self.off[p]) + int(self.m[p])]
         return v.view((s,) + tuple(shp[1:])) if len(shp) else v
+
+
+class StagedRS:
+    """Copy-engine-staged reduce-scatter over a plan: ``stage`` holds R bf16
+    tensors (rank r's staging buffer of R slots of ``slot_stride`` elements,
+    e.g. the rank's vacated gathered buffer with slot_stride = S).
+    ``stage_dma()`` moves every rank's slices into the slots on the DMA
+    engines (host-synchronous); ``fold()`` reduces the slots into the plan's
+    fp32 arenas on the compute units (asynchronous)."""
+
+    def __init__(self, plan: Plan, stage, slot_stride: int = 0):
+        if len(stage) != plan.R:
+            raise TideError(-1, "need R staging buffers")
+        self.plan = plan
+        self.slot_stride = int(slot_stride) if slot_stride else int(plan.S)
+        for r, t in enumerate(stage):
+            _require(t, torch.bfloat16, "stage[%d]" % r)
+            if t.numel() < plan.R * self.slot_stride:
+                raise TideError(-1, "stage[%d] holds %d elements, need R*slot_stride=%d"
+                                % (r, t.numel(), plan.R * self.slot_stride))
+        self.stage = list(stage)
+        self.h_stage = np.array([t.data_ptr() for t in stage], dtype=np.uint64)
+        self.d_stage = torch.from_numpy(self.h_stage.view(np.int64).copy()).to(stage[0].device)
+
+    def stage_dma(self, stream=None) -> None:
+        tide_rs_stage_dma(self.plan.blob, self.h_stage, self.slot_stride, stream)
+
+    def fold(self, order: str = "fixed", max_workgroups: int = 0, stream=None) -> None:
+        tide_rs_fold_staged(self.plan.blob, self.plan.d_blob, ORDERS[order], self.h_stage,
+                            self.d_stage, self.slot_stride, max_workgroups, stream)

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtide.so")
-SOURCES = ["plan.cpp", "rs.hip", "ag.hip"]
+SOURCES = ["plan.cpp", "rs.hip", "ag.hip", "dma.cpp"]
+LIBS = ["-L/opt/rocm/lib", "-lhsa-runtime64"]  # ROCr, for the copy engines
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,7 +30,7 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + LIBS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -28,6 +28,7 @@
 #include <cstring>
 
 #include "plan_format.h"
+#include "stage_check.h"
 #include "tide.h"
 
 using namespace tide;
@@ -127,6 +128,31 @@ __device__ __forceinline__ const uint16_t* at(const uint64_t* gp, int q, int64_t
     return reinterpret_cast<const uint16_t*>(base + (uint32_t)(2 * e));
 }
 
+// Where a tile reads rank q's value of its element e.
+// In place: rank q's gradient tensor of the tile's param, flat index j0 + e.
+struct GradSrc {
+    const uint64_t* gp;  // the param's R gradient pointers
+    int64_t j0;
+    __device__ __forceinline__ const uint16_t* vec(int q, int e) const { return at(gp, q, j0, e); }
+    __device__ __forceinline__ const uint16_t* one(int q, int e) const {
+        return src_of(gp, q) + j0 + e;
+    }
+};
+
+// Staged: slot q of the output rank's staging buffer, which holds rank q's
+// slice of every param at the same offsets as the rank's fp32 arena, so the
+// element sits at arena offset o0 + e of every slot.
+struct SlotSrc {
+    const char* base;  // staging buffer of the tile's rank + 2 * o0
+    int64_t stride;    // bytes from one slot to the next
+    __device__ __forceinline__ const uint16_t* vec(int q, int e) const {
+        return reinterpret_cast<const uint16_t*>(base + q * stride + (uint32_t)(2 * e));
+    }
+    __device__ __forceinline__ const uint16_t* one(int q, int e) const {
+        return reinterpret_cast<const uint16_t*>(base + q * stride) + e;
+    }
+};
+
 // Store a lane's 8 fp32 results so that each store instruction of the wave
 // writes one contiguous 1 KB run.  Lane l holds elements [8l, 8l+8) of the
 // wave's 512-element chunk; written as two 16-byte stores per lane, each
@@ -175,14 +201,14 @@ __device__ __forceinline__ void store8_unaligned(float* __restrict__ out, int e,
 // Vector tile, fixed rank order.  Each lane owns U chunks of 8 elements
 // (kBlock*8 apart) and issues U*RB 16-byte loads before it adds anything.
 // RB ranks are loaded per batch; EXACT means R is a multiple of RB (no
-// per-rank guard).  gp: the R source pointers of this param (uniform); j0:
-// first flat index; len % 8 == 0.  The loop bounds are uniform over the
+// per-rank guard).  src: where the tile's R source runs are (uniform, every
+// run 16-byte aligned); len % 8 == 0.  The loop bounds are uniform over the
 // workgroup, so every lane of a wave reaches the LDS exchange of the
 // contiguous store; a lane past len re-reads the tile's first elements
 // instead of branching around its loads (its results are never stored).
-template <int RB, bool EXACT, int U, bool NTL, bool NTS>
-__device__ __forceinline__ void rs_vec_fixed(const uint64_t* __restrict__ gp, int R, int64_t j0,
-                                             int len, float* __restrict__ out, float* lds_wave) {
+template <int RB, bool EXACT, int U, bool NTL, bool NTS, class Src>
+__device__ __forceinline__ void rs_vec_fixed(const Src& src, int R, int len,
+                                             float* __restrict__ out, float* lds_wave) {
     constexpr int kStep = kBlock * kVec;
     const bool out16 = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
     const int wave0 = (int)(threadIdx.x & ~63) * kVec;  // this wave's offset in a step
@@ -203,7 +229,7 @@ __device__ __forceinline__ void rs_vec_fixed(const uint64_t* __restrict__ gp, in
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int b = 0; b < RB; ++b)
-                    if (EXACT || b < nb) v[u][b] = load16<NTL>(at(gp, b, j0, e[u]));
+                    if (EXACT || b < nb) v[u][b] = load16<NTL>(src.vec(b, e[u]));
             // keep the whole batch of loads in flight before any add
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -221,7 +247,7 @@ __device__ __forceinline__ void rs_vec_fixed(const uint64_t* __restrict__ gp, in
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int b = 0; b < RB; ++b)
-                    if (EXACT || b < nb) v[u][b] = load16<NTL>(at(gp, q0 + b, j0, e[u]));
+                    if (EXACT || b < nb) v[u][b] = load16<NTL>(src.vec(q0 + b, e[u]));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -241,12 +267,12 @@ __device__ __forceinline__ void rs_vec_fixed(const uint64_t* __restrict__ gp, in
 
 // Element-wise tile (unaligned heads and tails, or sources whose 16-byte
 // phases differ between ranks): one element per lane, same order.
-__device__ __forceinline__ void rs_scalar_fixed(const uint64_t* __restrict__ gp, int R, int64_t j0,
-                                                int len, float* __restrict__ out) {
+template <class Src>
+__device__ __forceinline__ void rs_scalar_fixed(const Src& src, int R, int len,
+                                                float* __restrict__ out) {
     for (int e = threadIdx.x; e < len; e += kBlock) {
-        const int64_t j = j0 + e;
-        float a = bf_one(load2(src_of(gp, 0) + j));
-        for (int q = 1; q < R; ++q) a = a + bf_one(load2(src_of(gp, q) + j));
+        float a = bf_one(load2(src.one(0, e)));
+        for (int q = 1; q < R; ++q) a = a + bf_one(load2(src.one(q, e)));
         store4(out + e, a);
     }
 }
@@ -314,9 +340,9 @@ __device__ __forceinline__ void widen8(float (&x)[8], u32x4 v) {
     x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
 }
 
-template <int LEVELS, bool NTL, bool NTS>
-__device__ __forceinline__ void rs_vec_tree(const uint64_t* __restrict__ gp, int R, int64_t j0,
-                                            int len, float* __restrict__ out, float* lds_wave) {
+template <int LEVELS, bool NTL, bool NTS, class Src>
+__device__ __forceinline__ void rs_vec_tree(const Src& src, int R, int len,
+                                            float* __restrict__ out, float* lds_wave) {
     constexpr int RB = 8;
     constexpr int kStep = kBlock * kVec;
     const bool out16 = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
@@ -331,7 +357,7 @@ __device__ __forceinline__ void rs_vec_tree(const uint64_t* __restrict__ gp, int
             const int nb = (R - q0) < RB ? (R - q0) : RB;
 #pragma unroll
             for (int b = 0; b < RB; ++b)
-                if (b < nb) v[b] = load16<NTL>(at(gp, q0 + b, j0, e));
+                if (b < nb) v[b] = load16<NTL>(src.vec(q0 + b, e));
 #pragma unroll
             for (int b = 0; b < RB; ++b)
                 if (b < nb) {
@@ -349,14 +375,13 @@ __device__ __forceinline__ void rs_vec_tree(const uint64_t* __restrict__ gp, int
     }
 }
 
-template <int LEVELS>
-__device__ __forceinline__ void rs_scalar_tree(const uint64_t* __restrict__ gp, int R, int64_t j0,
-                                               int len, float* __restrict__ out) {
+template <int LEVELS, class Src>
+__device__ __forceinline__ void rs_scalar_tree(const Src& src, int R, int len,
+                                               float* __restrict__ out) {
     for (int e = threadIdx.x; e < len; e += kBlock) {
-        const int64_t j = j0 + e;
         TreeStack<LEVELS, 1> st;
         for (int q = 0; q < R; ++q) {
-            float x[1] = {bf_one(load2(src_of(gp, q) + j))};
+            float x[1] = {bf_one(load2(src.one(q, e)))};
             st.push(x, q);
         }
         float a[1];
@@ -378,11 +403,11 @@ __global__ __launch_bounds__(kBlock) void rs_tree_kernel(const RsTile* __restric
         if (census && threadIdx.x == 0) census[t] = hw_cu_id();
         const RsTile tile = tiles[t];
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
-        const uint64_t* gp = gptr + (int64_t)tile.p * R;
+        const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
         if (tile.kind == kRsVec)
-            rs_vec_tree<LEVELS, NTL, NTS>(gp, R, tile.j0, tile.len, out, lds_wave);
+            rs_vec_tree<LEVELS, NTL, NTS>(src, R, tile.len, out, lds_wave);
         else if (tile.kind == kRsScalar)
-            rs_scalar_tree<LEVELS>(gp, R, tile.j0, tile.len, out);
+            rs_scalar_tree<LEVELS>(src, R, tile.len, out);
         else
             rs_pad(tile.len, out);
     }
@@ -401,11 +426,68 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
         if (census && threadIdx.x == 0) census[t] = hw_cu_id();
         const RsTile tile = tiles[t];
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
-        const uint64_t* gp = gptr + (int64_t)tile.p * R;
+        const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
         if (tile.kind == kRsVec)
-            rs_vec_fixed<RB, EXACT, U, NTL, NTS>(gp, R, tile.j0, tile.len, out, lds_wave);
+            rs_vec_fixed<RB, EXACT, U, NTL, NTS>(src, R, tile.len, out, lds_wave);
         else if (tile.kind == kRsScalar)
-            rs_scalar_fixed(gp, R, tile.j0, tile.len, out);
+            rs_scalar_fixed(src, R, tile.len, out);
+        else
+            rs_pad(tile.len, out);
+    }
+}
+
+// ---- fold of staged slots
+//
+// The copy engines have moved rank q's slice of every param of rank r's
+// shard into slot q of rank r's staging buffer (stage[r] + q * stride bytes,
+// laid out like rank r's fp32 arena), so a tile's R runs are the slots at
+// its arena offset o0.  Same tiles, rank order and bits as the in-place
+// kernels.  vec_ok: every staging buffer and the slot stride are 16-byte
+// aligned; a vector tile whose o0 is not a multiple of 8 goes element-wise.
+__device__ __forceinline__ SlotSrc slot_src(const uint64_t* stage, int64_t stride,
+                                            const RsTile& tile) {
+    return SlotSrc{reinterpret_cast<const char*>(stage[tile.r]) + 2 * tile.o0, stride};
+}
+
+template <int RB, bool EXACT, int U, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void rs_fold_kernel(const RsTile* __restrict__ tiles,
+                                                         int64_t ntiles,
+                                                         const uint64_t* __restrict__ stage,
+                                                         int64_t stride, int vec_ok,
+                                                         const uint64_t* __restrict__ obase,
+                                                         int R) {
+    __shared__ float lds[kBlock * kVec];
+    float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const RsTile tile = tiles[tile_of(b, ntiles)];
+        float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
+        const SlotSrc src = slot_src(stage, stride, tile);
+        if (tile.kind == kRsVec && vec_ok && (tile.o0 & 7) == 0)
+            rs_vec_fixed<RB, EXACT, U, NTL, NTS>(src, R, tile.len, out, lds_wave);
+        else if (tile.kind != kRsPad)
+            rs_scalar_fixed(src, R, tile.len, out);
+        else
+            rs_pad(tile.len, out);
+    }
+}
+
+template <int LEVELS, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void rs_fold_tree_kernel(const RsTile* __restrict__ tiles,
+                                                              int64_t ntiles,
+                                                              const uint64_t* __restrict__ stage,
+                                                              int64_t stride, int vec_ok,
+                                                              const uint64_t* __restrict__ obase,
+                                                              int R) {
+    __shared__ float lds[kBlock * kVec];
+    float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const RsTile tile = tiles[tile_of(b, ntiles)];
+        float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
+        const SlotSrc src = slot_src(stage, stride, tile);
+        if (tile.kind == kRsVec && vec_ok && (tile.o0 & 7) == 0)
+            rs_vec_tree<LEVELS, NTL, NTS>(src, R, tile.len, out, lds_wave);
+        else if (tile.kind != kRsPad)
+            rs_scalar_tree<LEVELS>(src, R, tile.len, out);
         else
             rs_pad(tile.len, out);
     }
@@ -453,6 +535,44 @@ RsKernel pick_tree(int R, uint32_t flags) {
     static_assert(kMaxRanks <= 4096, "13 levels cover R <= 8191");
     if (R <= 127) return pick_tree_nt<7>(flags);
     return pick_tree_nt<13>(flags);
+}
+
+typedef void (*FoldKernel)(const RsTile*, int64_t, const uint64_t*, int64_t, int, const uint64_t*,
+                           int);
+
+template <int RB, bool EXACT, int U>
+FoldKernel pick_fold_nt(uint32_t flags) {
+    const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
+    if (ntl && nts) return rs_fold_kernel<RB, EXACT, U, true, true>;
+    if (ntl) return rs_fold_kernel<RB, EXACT, U, true, false>;
+    if (nts) return rs_fold_kernel<RB, EXACT, U, false, true>;
+    return rs_fold_kernel<RB, EXACT, U, false, false>;
+}
+
+// Same rank batching as the in-place kernels.
+FoldKernel pick_fold(int R, uint32_t flags) {
+    switch (R) {
+        case 1: return pick_fold_nt<1, true, 4>(flags);
+        case 2: return pick_fold_nt<2, true, 4>(flags);
+        case 4: return pick_fold_nt<4, true, 4>(flags);
+        default: break;
+    }
+    if (R % 8 == 0) return pick_fold_nt<8, true, 1>(flags);
+    return pick_fold_nt<8, false, 1>(flags);
+}
+
+template <int LEVELS>
+FoldKernel pick_fold_tree_nt(uint32_t flags) {
+    const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
+    if (ntl && nts) return rs_fold_tree_kernel<LEVELS, true, true>;
+    if (ntl) return rs_fold_tree_kernel<LEVELS, true, false>;
+    if (nts) return rs_fold_tree_kernel<LEVELS, false, true>;
+    return rs_fold_tree_kernel<LEVELS, false, false>;
+}
+
+FoldKernel pick_fold_tree(int R, uint32_t flags) {
+    if (R <= 127) return pick_fold_tree_nt<7>(flags);
+    return pick_fold_tree_nt<13>(flags);
 }
 
 }  // namespace
@@ -516,6 +636,45 @@ extern "C" tide_status tide_rs_bf16_to_fp32_tiles(const void* h_plan, const void
                                                   tide_stream_t stream) {
     if (tile_count < 0) return TIDE_EINVAL;
     return launch_rs(h_plan, d_plan, order, tile_begin, tile_count, max_workgroups, stream);
+}
+
+extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_plan, int32_t order,
+                                           const uint64_t* h_stage, const uint64_t* d_stage,
+                                           int64_t slot_stride, int32_t max_workgroups,
+                                           tide_stream_t stream) {
+    if (!h_plan || !d_plan || !d_stage) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (order != 0 && order != 1) return TIDE_EINVAL;
+    if (max_workgroups < 0) return TIDE_EINVAL;
+    bool vec_ok = false;
+    tide_status st = check_stage(h_plan, h_stage, slot_stride, &vec_ok);
+    if (st != TIDE_OK) return st;
+    if (reinterpret_cast<uintptr_t>(d_plan) % 16 || reinterpret_cast<uintptr_t>(d_stage) % 8)
+        return TIDE_EALIGN;
+    if (h.n_rs_tiles == 0) return TIDE_OK;
+
+    const uint8_t* d = static_cast<const uint8_t*>(d_plan);
+    const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
+    const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
+    int R = h.R;
+    int vec = vec_ok ? 1 : 0;
+    int64_t stride = 2 * slot_stride;
+    FoldKernel k = order == 0 ? pick_fold(R, h.flags) : pick_fold_tree(R, h.flags);
+    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : h.n_rs_tiles;
+    for (int64_t b = 0; b < h.n_rs_tiles; b += per_launch) {
+        const RsTile* tiles = all + b;
+        int64_t ntiles = per_launch < h.n_rs_tiles - b ? per_launch : h.n_rs_tiles - b;
+        int64_t grid = ntiles;
+        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+        if (grid > INT_MAX) grid = INT_MAX;
+        void* args[] = {&tiles, &ntiles, &d_stage, &stride, &vec, &obase, &R};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return TIDE_EHIP;
+    }
+    return TIDE_OK;
 }
 
 extern "C" tide_status tide_rs_bf16_to_fp32_census(const void* h_plan, const void* d_plan,

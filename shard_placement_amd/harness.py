@@ -143,3 +143,20 @@ def setup(w: configs.Workload, device="cuda", with_rs=True, with_ag=True, guard:
                        gathered=st.gathered, full=st.full, align=align, rs_tile=rs_tile,
                        ag_tile=ag_tile, flags=flags, launch_mib=launch_mib)
     return st
+
+
+def stage_buffers(st: Setup, slot_stride: int = 0, rank_layout: str = "packed",
+                  offset: int = 0) -> List[torch.Tensor]:
+    """R staging buffers for the copy-engine-staged reduce-scatter, each R
+    slots of slot_stride (default S) bf16 elements, filled with the 0xFFFF
+    sentinel; ``offset`` elements into their allocation (to test unaligned
+    slots)."""
+    w = st.w
+    stride = slot_stride or st.S
+    n = w.R * stride
+    rows = _rank_rows(w.R, n + offset, torch.bfloat16, st.device, rank_layout == "packed")
+    out = []
+    for r in range(w.R):
+        rows[r].view(torch.int16).fill_(BF16_SENTINEL)
+        out.append(rows[r][offset:offset + n])
+    return out

@@ -313,3 +313,48 @@ def test_ag_realigning_tiles_for_shifted_slots(gmis):
     for t in ag:
         if t["kind"] != 3:
             assert t["len"] < 64
+
+
+def test_staging_validation_before_touching_the_gpu():
+    """The copy-engine-staged reduce-scatter and the copy-engine placement
+    reject bad staging buffers and plans on the host, before any GPU call."""
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S)
+    L = _lib.lib()
+    blob, _ = api.tide_desc_build(SHAPES, R, g, o, None, None)
+    fake_dev = ctypes.c_void_p(1 << 44)
+    span = ((2 * R * S + 4095) // 4096 + 1) * 4096
+    good = np.array([(1 << 45) + r * span for r in range(R)], dtype=np.uint64)
+
+    def fold(stage, stride=S, order=0, max_wg=0, d_stage=1 << 46, plan=blob):
+        arr = stage.ctypes.data if stage is not None else None
+        return L.tide_rs_fold_staged(plan.ctypes.data, fake_dev, order, arr, ctypes.c_void_p(d_stage),
+                                     stride, max_wg, None)
+
+    def stage_dma(stage, stride=S, plan=blob):
+        arr = stage.ctypes.data if stage is not None else None
+        return L.tide_rs_stage_dma(plan.ctypes.data, arr, stride, None)
+
+    for call in (fold, stage_dma):
+        assert call(good, stride=S - 1) == -1                     # slots shorter than S
+        assert call(None) == -1                                   # no staging array
+        bad = good.copy(); bad[2] = 0
+        assert call(bad) == -1                                    # NULL staging buffer
+        bad = good.copy(); bad[1] += 1
+        assert call(bad) == -2                                    # odd bf16 address
+        bad = good.copy(); bad[3] = bad[2] + 2 * S
+        assert call(bad) == -3                                    # two ranks' buffers overlap
+        bad = good.copy(); bad[0] = g[1] - 2
+        assert call(bad) == -3                                    # over a gradient tensor
+        bad = good.copy(); bad[0] = o[2] + 8
+        assert call(bad) == -3                                    # over an output arena
+    assert fold(good, order=2) == -1
+    assert fold(good, max_wg=-1) == -1
+    assert fold(good, d_stage=(1 << 46) + 4) == -2                # misaligned device array
+    ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
+    assert fold(good, plan=ag_blob) == -6 and stage_dma(good, plan=ag_blob) == -6
+    junk = np.zeros(4096, np.uint8)
+    assert fold(good, plan=junk) == -7 and stage_dma(good, plan=junk) == -7
+    assert L.tide_ag_place_dma(blob.ctypes.data, None) == -6     # no placement pointers
+    assert L.tide_ag_place_dma(junk.ctypes.data, None) == -7

@@ -26,15 +26,21 @@ def _wl(shapes, R, key=300, sigma=1.0):
                             shapes=shapes, sigma=sigma)
 
 
-@pytest.mark.parametrize("engine", ["cu", "sdma", "sdma-any"])
+def _place(plan, engine):
+    if engine == "cu":
+        plan.ag()
+    elif engine == "dma":
+        plan.ag_dma()
+    else:
+        plan.ag_sdma(engine_only=(engine == "sdma"))
+
+
+@pytest.mark.parametrize("engine", ["cu", "sdma", "sdma-any", "dma"])
 def test_tiny_workload_bitwise(engine):
     w = configs.get(1)
     gu.say("tiny ag", engine)
     st = harness.setup(w, with_rs=False, gen_device="cpu")
-    if engine == "cu":
-        st.plan.ag()
-    else:
-        st.plan.ag_sdma(engine_only=(engine == "sdma"))
+    _place(st.plan, engine)
     torch.cuda.synchronize()
     gu.check_ag_full(st)
 
@@ -51,21 +57,21 @@ CASES = [
 
 
 @pytest.mark.parametrize("R,shapes", CASES, ids=[str(c[0]) for c in CASES])
-@pytest.mark.parametrize("engine", ["cu", "sdma"])
+@pytest.mark.parametrize("engine", ["cu", "sdma", "dma"])
 @pytest.mark.parametrize("tile", [0, 2048])
 def test_ragged_shapes_bitwise(R, shapes, engine, tile):
-    if engine == "sdma" and tile:
-        pytest.skip("the copy-engine path has no tiles")
+    if engine != "cu" and tile:
+        pytest.skip("the copy-engine paths have no tiles")
     w = _wl(shapes, R, key=310 + R)
     gu.say("ragged ag", R, shapes, engine, tile)
     st = harness.setup(w, with_rs=False, ag_tile=tile)
-    st.plan.ag() if engine == "cu" else st.plan.ag_sdma()
+    _place(st.plan, engine)
     torch.cuda.synchronize()
     gu.check_ag_full(st)
 
 
 @pytest.mark.parametrize("gshift", [1, 2, 3, 4, 5, 7])
-@pytest.mark.parametrize("engine", ["cu", "sdma"])
+@pytest.mark.parametrize("engine", ["cu", "sdma", "dma"])
 def test_unaligned_gathered_buffer(gshift, engine):
     """The gathered buffer starts gshift elements into an allocation, so
     slots and full tensors disagree in 16-byte (or 4-byte) phase."""
@@ -81,7 +87,7 @@ def test_unaligned_gathered_buffer(gshift, engine):
     full = synth.views(fa[16:16 + n], shapes)
     plan = api.Plan(shapes, R, gathered=gathered, full=full)
     gu.say("unaligned ag", gshift, engine)
-    plan.ag() if engine == "cu" else plan.ag_sdma()
+    _place(plan, engine)
     torch.cuda.synchronize()
     want = [np.full(gu.numel(s), gu.SENT16, np.uint16) for s in shapes]
     oracle.ag(shapes, R, gu.bits16(gathered), out=want)
@@ -116,10 +122,10 @@ def test_fuzz_random_placements(seed):
     gu.say("fuzz ag", seed, R, shapes, align, gshift, tile)
     want = [np.full(gu.numel(s), gu.SENT16, np.uint16) for s in shapes]
     oracle.ag(shapes, R, gu.bits16(gathered), align=align, out=want)
-    for engine in ("cu", "sdma"):
+    for engine in ("cu", "sdma", "dma"):
         fa.view(torch.int16).fill_(-1)
         plan = api.Plan(shapes, R, gathered=gathered, full=full, align=align, ag_tile=tile)
-        plan.ag() if engine == "cu" else plan.ag_sdma()
+        _place(plan, engine)
         torch.cuda.synchronize()
         for p in range(len(shapes)):
             gu.assert_bits_equal(gu.bits16(full[p]), want[p], "%s full[%d]" % (engine, p))
@@ -174,10 +180,10 @@ def test_random_bit_patterns_round_trip():
     n = synth.arena_numel(shapes)
     fa = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     full = synth.views(fa, shapes)
-    for engine in ("cu", "sdma"):
+    for engine in ("cu", "sdma", "dma"):
         fa.view(torch.int16).fill_(0x1234)
         plan = api.Plan(shapes, R, gathered=gathered, full=full)
-        plan.ag() if engine == "cu" else plan.ag_sdma()
+        _place(plan, engine)
         torch.cuda.synchronize()
         for p, t in enumerate(fulls):
             assert torch.equal(full[p].cpu().view(torch.int16), t.view(torch.int16)), (engine, p)
@@ -205,9 +211,10 @@ def test_full_size_placement(key):
     w = configs.get(key)
     gu.say("full-size ag", w.name)
     st = harness.setup(w, with_rs=False, guard=64)
-    for engine in ("cu", "sdma"):
+    for engine in ("cu", "sdma", "dma"):
         st.full_arena.view(torch.int16).fill_(-1)
-        st.plan.ag() if engine == "cu" else st.plan.ag_sdma()
+        gu.say("full-size ag", w.name, engine)
+        _place(st.plan, engine)
         torch.cuda.synchronize()
         gu.say("oracle ag compare", w.name, engine)
         gu.check_ag_full(st)
