@@ -79,6 +79,96 @@ def read_traffic(kernel: str, workload: str, sources) -> Optional[float]:
         return None
 
 
+def _wall(fn, reps: int = 3) -> float:
+    """Median wall time (ms) of a host-synchronous call."""
+    import torch
+
+    fn()
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    return sorted(ts)[len(ts) // 2]
+
+
+def dma_placement_leg(st, agb: int) -> dict:
+    """Placement on the DMA engines through ROCr (engine-pinned 1-D copies,
+    one per (param, rank) run), checked against the compute-unit placement."""
+    import torch
+
+    from shard_placement_amd import api
+
+    st.plan.ag()
+    torch.cuda.synchronize()
+    ref = [f.clone() for f in st.full]
+    ms = _wall(st.plan.ag_dma)
+    same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, st.full))
+    del ref
+    return {"engines": api.tide_dma_engine_count(), "ms": round(ms, 4),
+            "GB/s": round(agb / (ms * 1e-3) / 1e9, 1), "same_bits": bool(same),
+            "copies": "one engine-pinned 1-D copy per (param, rank) run, host-synchronous"}
+
+
+def staged_leg(st, rsb: int, fused_ms: float, reps: int = 3) -> dict:
+    """Copy-engine-staged reduce-scatter: the DMA engines copy every rank's
+    slice of every shard into per-rank staging slots, then a kernel folds
+    the slots.  With Slot-Reuse the slots are the ranks' vacated gathered
+    buffers and the fp32 shards go to arenas of their own; otherwise the
+    staging buffers are allocated here.  Also times a single-wave GEMM while
+    the engines stage (the compute units stay free for it)."""
+    import torch
+
+    from shard_placement_amd import api, harness, probe
+
+    w = st.w
+    if st.vacated is not None:
+        out = [torch.empty(st.S, dtype=torch.float32, device="cuda") for _ in range(w.R)]
+        plan = api.Plan(w.shapes, w.R, grads=st.grads, out=out)
+        stage = [v[: w.R * st.S] for v in st.vacated]
+        where = "vacated gathered buffers (slot stride S)"
+    else:
+        out = st.out
+        plan = st.plan
+        stage = harness.stage_buffers(st)
+        where = "staging buffers of R*S bf16 per rank"
+    st.plan.rs()  # the fused result, for the bit comparison
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    srs = api.StagedRS(plan, stage)
+    stage_ms = _wall(srs.stage_dma, reps)
+    srs.fold()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        srs.fold()
+    e1.record()
+    torch.cuda.synchronize()
+    fold_ms = e0.elapsed_time(e1) / reps
+    same = all(torch.equal(a[: st.S].view(torch.int32), b[: st.S].view(torch.int32))
+               for a, b in zip(out, ref))
+    del ref
+    # a single-wave GEMM train while the engines stage
+    g = probe.gemm_during(lambda: srs.stage_dma(), stage_ms)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    staged_bytes = 2 * w.R * w.numel()
+    rec = {"staging": where, "engines": api.tide_dma_engine_count(),
+           "stage_ms": round(stage_ms, 3), "stage_copy_gbps": round(staged_bytes / (stage_ms * 1e-3) / 1e9, 1),
+           "fold_ms": round(fold_ms, 4), "fold_gbps": round(rsb / (fold_ms * 1e-3) / 1e9, 1),
+           "total_ms": round(stage_ms + fold_ms, 3), "fused_ms": round(fused_ms, 4),
+           "fold_cu_ms": round(n_cu * fold_ms, 1), "fused_cu_ms": round(n_cu * fused_ms, 1),
+           "stage_cu_ms": 0.0, "same_bits_as_fused": bool(same)}
+    rec.update(g)
+    del srs, stage, plan
+    if st.vacated is not None:
+        st.plan.rs()  # staging overwrote the Slot-Reuse arenas inside the vacated buffers
+        torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
 def stock_leg(st, rsb: int, agb: int, reps: int = 3) -> dict:
     """Time the one-GPU analog of stock FSDP2's layout conversion (pack the
     ranks' gradients into a rank-major fp32 buffer, add in rank order, copy
@@ -196,6 +286,8 @@ def main():
                     help="skip even the default-configuration GEMM probe")
     ap.add_argument("--no-sdma", action="store_true", help="skip timing the copy-engine placement")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a HIP graph")
+    ap.add_argument("--no-staged", action="store_true",
+                    help="skip the copy-engine legs (DMA placement, copy-engine-staged RS)")
     ap.add_argument("--no-stock", action="store_true",
                     help="skip timing the stock-FSDP2 analog (pack, add, copy out in torch ops)")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -319,6 +411,13 @@ def main():
                                                               dict(sorted(per_xcc.items()))))
     del census
 
+    dma_rec = staged_rec = None
+    if not args.no_staged:
+        dma_rec = dma_placement_leg(st, agb)
+        log("placement on the DMA engines", dma_rec)
+        staged_rec = staged_leg(st, rsb, rs_avg)
+        log("copy-engine-staged RS", staged_rec)
+
     stock_rec = None
     if not args.no_stock:
         stock_rec = stock_leg(st, rsb, agb)
@@ -391,6 +490,8 @@ def main():
         "rs_cus": cus_measured,
         "rs_cus_per_xcc": {str(k): v for k, v in sorted(per_xcc.items())},
         "rs_cu_ms": round(cus_measured * rs_avg, 1),
+        "ag_dma": dma_rec,
+        "staged_rs": staged_rec,
         "stock_analog": stock_rec,
         "probe": probe,
         # per kernel launch: one reduce-scatter call is n_launch launches of

@@ -108,3 +108,33 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
             torch.cuda.synchronize()
             api.tide_stream_destroy(rs_stream)
     return out
+
+
+def gemm_during(host_call, expect_ms: float, M: int = 4096, N: int = 4096, K: int = 8192) -> Dict:
+    """Median time of the single-wave GEMM alone (trains before and after,
+    pooled), and while ``host_call`` (a host-synchronous call that keeps the
+    DMA engines busy for about expect_ms, e.g. copy-engine staging) runs: a
+    GEMM train of about half that length is queued on its own stream just
+    before the call."""
+    dev = torch.device("cuda")
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    s = torch.cuda.Stream()
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    alone = _gemm_train(a, b, c, s, 30)
+    torch.cuda.synchronize()
+    t0 = _median([e0.elapsed_time(e1) for e0, e1 in alone])
+    n = max(4, min(400, int(0.5 * expect_ms / t0)))
+    conc = _gemm_train(a, b, c, s, n)
+    host_call()
+    torch.cuda.synchronize()
+    t1 = _median([e0.elapsed_time(e1) for e0, e1 in conc])
+    after = _gemm_train(a, b, c, s, 30)
+    torch.cuda.synchronize()
+    t0 = _median([e0.elapsed_time(e1) for e0, e1 in alone + after])
+    return {"gemm_alone_ms": round(t0, 4), "gemm_during_staging_ms": round(t1, 4),
+            "gemm_during_staging": n,
+            "gemm_slowdown_during_staging_pct": round(100.0 * (t1 / t0 - 1.0), 2)}
