@@ -169,6 +169,65 @@ def staged_leg(st, rsb: int, fused_ms: float, reps: int = 3) -> dict:
     return rec
 
 
+def pipeline_leg(st, fused_ms: float) -> dict:
+    """Two-phase pipeline emulation: each phase alone over the whole layer,
+    then the two-stream ring for several chunk sizes (in launches of the
+    plan's size), ring depths and phase-2 engines; checks the bits of the
+    pipelined result against the in-place reduce-scatter."""
+    import torch
+
+    from shard_placement_amd import api, pipeline
+
+    plan = st.plan
+    n, T = int(plan.info.rs_tiles), int(plan.info.rs_tile_elems)
+    L = int(plan.info.rs_launch_tiles) or n
+    plan.rs()
+    torch.cuda.synchronize()
+    ref = [o[: st.S].clone() for o in st.out]
+
+    def ev_time(fn, reps=2):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    full = torch.empty(n * T, dtype=torch.float32, device="cuda")
+    t1 = ev_time(lambda: api.tide_rs_tiles_to_stage(plan.blob, plan.d_blob, 0, n, full))
+    t2 = {"cu": ev_time(lambda: api.tide_rs_stage_to_shards(plan.blob, plan.d_blob, 0, n, full)),
+          "sdma": ev_time(lambda: api.tide_rs_stage_to_shards_sdma(plan.blob, 0, n, full), reps=1)}
+    del full
+    torch.cuda.empty_cache()
+    runs = []
+    same = True
+    for phase2 in ("cu", "sdma"):
+        for mult, depth in ((0.25, 2), (1, 1), (1, 2), (1, 4), (4, 2)):
+            chunk = max(1, int(L * mult))
+            tp = pipeline.TwoPhase(plan, chunk, depth, phase2)
+            try:
+                t = ev_time(tp.run, reps=1 if phase2 == "sdma" else 2)
+            finally:
+                tp.close()
+            same = same and all(torch.equal(o[: st.S].view(torch.int32), r.view(torch.int32))
+                                for o, r in zip(st.out, ref))
+            serial = t1 + t2[phase2]
+            runs.append({"phase2": phase2, "chunk_tiles": chunk, "depth": depth,
+                         "staging_mib": round(tp.staging_bytes / 2 ** 20, 1), "ms": round(t, 3),
+                         "overlap": round((serial - t) / min(t1, t2[phase2]), 3)})
+            del tp
+    del ref
+    torch.cuda.empty_cache()
+    return {"phase1_ms": round(t1, 4), "phase2_cu_ms": round(t2["cu"], 4),
+            "phase2_sdma_ms": round(t2["sdma"], 3), "fused_ms": round(fused_ms, 4),
+            "layer_staging_mib": round(n * T * 4 / 2 ** 20, 1), "runs": runs,
+            "same_bits_as_fused": bool(same),
+            "overlap_def": "(phase1 alone + phase2 alone - pipelined) / min(phase1, phase2)"}
+
+
 def stock_leg(st, rsb: int, agb: int, reps: int = 3) -> dict:
     """Time the one-GPU analog of stock FSDP2's layout conversion (pack the
     ranks' gradients into a rank-major fp32 buffer, add in rank order, copy
@@ -288,6 +347,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step as a HIP graph")
     ap.add_argument("--no-staged", action="store_true",
                     help="skip the copy-engine legs (DMA placement, copy-engine-staged RS)")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the two-phase pipeline emulation leg")
     ap.add_argument("--no-stock", action="store_true",
                     help="skip timing the stock-FSDP2 analog (pack, add, copy out in torch ops)")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -418,6 +479,11 @@ def main():
         staged_rec = staged_leg(st, rsb, rs_avg)
         log("copy-engine-staged RS", staged_rec)
 
+    pipe_rec = None
+    if not args.no_pipeline:
+        pipe_rec = pipeline_leg(st, rs_avg)
+        log("two-phase pipeline", pipe_rec)
+
     stock_rec = None
     if not args.no_stock:
         stock_rec = stock_leg(st, rsb, agb)
@@ -492,6 +558,7 @@ def main():
         "rs_cu_ms": round(cus_measured * rs_avg, 1),
         "ag_dma": dma_rec,
         "staged_rs": staged_rec,
+        "pipeline": pipe_rec,
         "stock_analog": stock_rec,
         "probe": probe,
         # per kernel launch: one reduce-scatter call is n_launch launches of

@@ -266,6 +266,38 @@ tide_status tide_rs_fold_staged(const void *h_plan, const void *d_plan, int32_t 
                                 int64_t slot_stride, int32_t max_workgroups,
                                 tide_stream_t stream);
 
+/* Two-phase pipeline, one GPU's emulation [Abstract: two-phase pipeline;
+ * Performance: reduce-scatter buffer nearly constant].  The reduce-scatter
+ * of a tile range [tile_begin, tile_begin + tile_count) is split into
+ *   phase 1, tide_rs_tiles_to_stage: the fixed-order reduction of those
+ *     tiles into a dense staging chunk: tile t's results (len fp32 values;
+ *     +0.0 for padding tiles) at stage + (t - tile_begin) * rs_tile_elems;
+ *   phase 2, tide_rs_stage_to_shards: a copy of those results to their
+ *     places in the fp32 arenas (the stand-in for the network phase that
+ *     delivers partial results to their owners).
+ * Phase 1 then phase 2 over every tile gives tide_rs_bf16_to_fp32's bits.
+ * stage: device memory of stage_elems >= tile_count * rs_tile_elems floats,
+ * 16-byte aligned, overlapping no gradient tensor or output arena (checked:
+ * TIDE_EOVERLAP).  A caller runs the phases on two streams with an event
+ * per chunk and a ring of staging chunks, so the staging memory is bounded
+ * by the ring, not the layer.  Asynchronous on `stream`; cut into launches
+ * of about the plan's launch size. */
+tide_status tide_rs_tiles_to_stage(const void *h_plan, const void *d_plan, int64_t tile_begin,
+                                   int64_t tile_count, float *stage, int64_t stage_elems,
+                                   int32_t max_workgroups, tide_stream_t stream);
+tide_status tide_rs_stage_to_shards(const void *h_plan, const void *d_plan, int64_t tile_begin,
+                                    int64_t tile_count, const float *stage, int64_t stage_elems,
+                                    int32_t max_workgroups, tide_stream_t stream);
+
+/* Phase 2 on the DMA engines instead of a kernel, with a copy engine's
+ * bandwidth (tens of GB/s, about a network link's) standing in for the
+ * network: one stream-ordered copy of the no-compute-unit kind per run of
+ * tiles contiguous in both the chunk and a rank's arena.  Asynchronous on
+ * `stream`; same arguments and checks as tide_rs_stage_to_shards. */
+tide_status tide_rs_stage_to_shards_sdma(const void *h_plan, int64_t tile_begin,
+                                         int64_t tile_count, const float *stage,
+                                         int64_t stage_elems, tide_stream_t stream);
+
 /* A stream whose kernels may run only on the first n_cu compute units of
  * the device's CU mask (hipExtStreamCreateWithCUMask; default priority), for
  * confining the reduce-scatter's workgroups to part of the chip next to

@@ -177,6 +177,39 @@ def tide_rs_fold_staged(h_plan: np.ndarray, d_plan: torch.Tensor, order: int,
           "tide_rs_fold_staged")
 
 
+def tide_rs_tiles_to_stage(h_plan: np.ndarray, d_plan: torch.Tensor, tile_begin: int,
+                           tile_count: int, stage: torch.Tensor, max_workgroups: int = 0,
+                           stream=None) -> None:
+    """Pipeline phase 1: reduce tiles [tile_begin, +tile_count) into the
+    dense fp32 staging chunk ``stage``."""
+    _require(stage, torch.float32, "stage")
+    check(_lib.lib().tide_rs_tiles_to_stage(h_plan.ctypes.data, d_plan.data_ptr(), int(tile_begin),
+                                            int(tile_count), stage.data_ptr(), stage.numel(),
+                                            int(max_workgroups), _stream(stream)),
+          "tide_rs_tiles_to_stage")
+
+
+def tide_rs_stage_to_shards(h_plan: np.ndarray, d_plan: torch.Tensor, tile_begin: int,
+                            tile_count: int, stage: torch.Tensor, max_workgroups: int = 0,
+                            stream=None) -> None:
+    """Pipeline phase 2: move a staging chunk's results into the arenas."""
+    _require(stage, torch.float32, "stage")
+    check(_lib.lib().tide_rs_stage_to_shards(h_plan.ctypes.data, d_plan.data_ptr(), int(tile_begin),
+                                             int(tile_count), stage.data_ptr(), stage.numel(),
+                                             int(max_workgroups), _stream(stream)),
+          "tide_rs_stage_to_shards")
+
+
+def tide_rs_stage_to_shards_sdma(h_plan: np.ndarray, tile_begin: int, tile_count: int,
+                                 stage: torch.Tensor, stream=None) -> None:
+    """Pipeline phase 2 on the copy engines (stream-ordered copies)."""
+    _require(stage, torch.float32, "stage")
+    check(_lib.lib().tide_rs_stage_to_shards_sdma(h_plan.ctypes.data, int(tile_begin),
+                                                  int(tile_count), stage.data_ptr(), stage.numel(),
+                                                  _stream(stream)),
+          "tide_rs_stage_to_shards_sdma")
+
+
 def tide_stream_create_cu_limited(n_cu: int) -> torch.cuda.ExternalStream:
     """A torch stream wrapping a HIP stream confined to the first n_cu CUs.
     Release it with tide_stream_destroy."""

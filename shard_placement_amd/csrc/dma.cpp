@@ -232,6 +232,89 @@ tide_status check_stage(const void* h_plan, const uint64_t* h_stage, int64_t slo
 
 }  // namespace tide
 
+namespace tide {
+
+bool overlaps_rs_buffers(const void* h_plan, uint64_t lo, uint64_t hi) {
+    if (lo >= hi) return false;
+    PlanHeader h;
+    read_header(h_plan, &h);
+    const uint8_t* b = static_cast<const uint8_t*>(h_plan);
+    const ParamDesc* ps = reinterpret_cast<const ParamDesc*>(b + h.off_params);
+    const uint64_t* gptr = reinterpret_cast<const uint64_t*>(b + h.off_gptr);
+    const uint64_t* obase = reinterpret_cast<const uint64_t*>(b + h.off_obase);
+    auto meets = [&](uint64_t a, uint64_t z) { return a < z && a < hi && lo < z; };
+    for (int32_t p = 0; p < h.P; ++p) {
+        ParamDesc d;
+        std::memcpy(&d, ps + p, sizeof d);
+        for (int32_t q = 0; q < h.R; ++q) {
+            const uint64_t g = gptr[(int64_t)p * h.R + q];
+            if (meets(g, g + 2ull * (uint64_t)d.n)) return true;
+        }
+    }
+    for (int32_t r = 0; r < h.R; ++r)
+        if (meets(obase[r], obase[r] + 4ull * (uint64_t)h.S)) return true;
+    return false;
+}
+
+tide_status check_pipeline(const void* h_plan, const void* d_plan, int64_t tile_begin,
+                           int64_t tile_count, const float* stage, int64_t stage_elems,
+                           int32_t max_workgroups, PlanHeader* h) {
+    if (!h_plan || !stage) return TIDE_EINVAL;
+    if (!read_header(h_plan, h)) return TIDE_EPLAN;
+    if (!h->has_rs) return TIDE_EUNSUPPORTED;
+    if (max_workgroups < 0) return TIDE_EINVAL;
+    if (tile_begin < 0 || tile_count < 0 || tile_begin > h->n_rs_tiles ||
+        tile_count > h->n_rs_tiles - tile_begin)
+        return TIDE_EINVAL;
+    if (tile_count > INT64_MAX / h->rs_tile || stage_elems < tile_count * h->rs_tile)
+        return TIDE_EINVAL;
+    if (reinterpret_cast<uintptr_t>(stage) % 16 || reinterpret_cast<uintptr_t>(d_plan) % 16)
+        return TIDE_EALIGN;
+    const uint64_t lo = reinterpret_cast<uint64_t>(stage);
+    if (overlaps_rs_buffers(h_plan, lo, lo + 4ull * (uint64_t)(tile_count * h->rs_tile)))
+        return TIDE_EOVERLAP;
+    return TIDE_OK;
+}
+
+}  // namespace tide
+
+extern "C" tide_status tide_rs_stage_to_shards_sdma(const void* h_plan, int64_t tile_begin,
+                                                    int64_t tile_count, const float* stage,
+                                                    int64_t stage_elems, tide_stream_t stream) {
+    PlanHeader h;
+    tide_status st = check_pipeline(h_plan, nullptr, tile_begin, tile_count, stage, stage_elems, 0,
+                                    &h);
+    if (st != TIDE_OK) return st;
+    const uint8_t* b = static_cast<const uint8_t*>(h_plan);
+    const RsTile* tiles = reinterpret_cast<const RsTile*>(b + h.off_rs);
+    const uint64_t* obase = reinterpret_cast<const uint64_t*>(b + h.off_obase);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // merge tiles into runs contiguous both in the chunk (every tile but the
+    // last of a run fills its T floats) and in the rank's arena
+    int64_t t = tile_begin;
+    const int64_t end = tile_begin + tile_count;
+    while (t < end) {
+        RsTile first;
+        std::memcpy(&first, tiles + t, sizeof first);
+        int64_t len = first.len;
+        int64_t u = t + 1;
+        while (u < end && len == (u - t) * (int64_t)h.rs_tile) {
+            RsTile nx;
+            std::memcpy(&nx, tiles + u, sizeof nx);
+            if (nx.r != first.r || nx.o0 != first.o0 + len) break;
+            len += nx.len;
+            ++u;
+        }
+        char* dst = reinterpret_cast<char*>(obase[first.r]) + 4 * first.o0;
+        const char* src = reinterpret_cast<const char*>(stage + (t - tile_begin) * h.rs_tile);
+        if (hipMemcpyAsync(dst, src, (size_t)(4 * len), hipMemcpyDeviceToDeviceNoCU, s) !=
+            hipSuccess)
+            return TIDE_EHIP;
+        t = u;
+    }
+    return TIDE_OK;
+}
+
 extern "C" tide_status tide_dma_engine_count(int32_t* count) {
     if (!count) return TIDE_EINVAL;
     const Engines* eng = nullptr;

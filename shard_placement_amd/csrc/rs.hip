@@ -493,6 +493,61 @@ __global__ __launch_bounds__(kBlock) void rs_fold_tree_kernel(const RsTile* __re
     }
 }
 
+// ---- two-phase pipeline
+//
+// Phase 1 reduces a range of tiles into a dense staging chunk (tile t of the
+// range at stage + t * T floats, T = the plan's tile size) instead of the
+// shard arenas; phase 2 moves a chunk's results to their places in the
+// arenas (the stand-in for the network phase that delivers partial results
+// to their owners).  Phase 1 computes exactly what the in-place kernel
+// computes; phase 2 is a copy, so phase 1 then phase 2 gives its bits.
+template <int RB, bool EXACT, int U, bool NTL, bool NTS>
+__global__ __launch_bounds__(kBlock) void rs_dense_kernel(const RsTile* __restrict__ tiles,
+                                                          int64_t ntiles,
+                                                          const uint64_t* __restrict__ gptr,
+                                                          float* __restrict__ stage, int64_t T,
+                                                          int R) {
+    __shared__ float lds[kBlock * kVec];
+    float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const int64_t t = tile_of(b, ntiles);
+        const RsTile tile = tiles[t];
+        float* out = stage + t * T;
+        const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
+        if (tile.kind == kRsVec)
+            rs_vec_fixed<RB, EXACT, U, NTL, NTS>(src, R, tile.len, out, lds_wave);
+        else if (tile.kind == kRsScalar)
+            rs_scalar_fixed(src, R, tile.len, out);
+        else
+            rs_pad(tile.len, out);
+    }
+}
+
+__device__ __forceinline__ f32x4 load16f(const float* p) {
+    return *(const TIDE_GLOBAL f32x4*)(p);
+}
+
+template <bool NTS>
+__global__ __launch_bounds__(kBlock) void rs_drain_kernel(const RsTile* __restrict__ tiles,
+                                                          int64_t ntiles,
+                                                          const float* __restrict__ stage,
+                                                          int64_t T,
+                                                          const uint64_t* __restrict__ obase) {
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const int64_t t = tile_of(b, ntiles);
+        const RsTile tile = tiles[t];
+        const float* src = stage + t * T;
+        float* dst = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
+        const int len = tile.len;
+        if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (len & 3) == 0) {
+            for (int e = threadIdx.x * 4; e < len; e += kBlock * 4)
+                store16<NTS>(dst + e, load16f(src + e));
+        } else {
+            for (int e = threadIdx.x; e < len; e += kBlock) store4(dst + e, src[e]);
+        }
+    }
+}
+
 typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int, uint32_t*);
 
 template <int RB, bool EXACT, int U>
@@ -535,6 +590,28 @@ RsKernel pick_tree(int R, uint32_t flags) {
     static_assert(kMaxRanks <= 4096, "13 levels cover R <= 8191");
     if (R <= 127) return pick_tree_nt<7>(flags);
     return pick_tree_nt<13>(flags);
+}
+
+typedef void (*DenseKernel)(const RsTile*, int64_t, const uint64_t*, float*, int64_t, int);
+
+template <int RB, bool EXACT, int U>
+DenseKernel pick_dense_nt(uint32_t flags) {
+    const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
+    if (ntl && nts) return rs_dense_kernel<RB, EXACT, U, true, true>;
+    if (ntl) return rs_dense_kernel<RB, EXACT, U, true, false>;
+    if (nts) return rs_dense_kernel<RB, EXACT, U, false, true>;
+    return rs_dense_kernel<RB, EXACT, U, false, false>;
+}
+
+DenseKernel pick_dense(int R, uint32_t flags) {
+    switch (R) {
+        case 1: return pick_dense_nt<1, true, 4>(flags);
+        case 2: return pick_dense_nt<2, true, 4>(flags);
+        case 4: return pick_dense_nt<4, true, 4>(flags);
+        default: break;
+    }
+    if (R % 8 == 0) return pick_dense_nt<8, true, 1>(flags);
+    return pick_dense_nt<8, false, 1>(flags);
 }
 
 typedef void (*FoldKernel)(const RsTile*, int64_t, const uint64_t*, int64_t, int, const uint64_t*,
@@ -672,6 +749,74 @@ extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_pla
         void* args[] = {&tiles, &ntiles, &d_stage, &stride, &vec, &obase, &R};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
                                        dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return TIDE_EHIP;
+    }
+    return TIDE_OK;
+}
+
+extern "C" tide_status tide_rs_tiles_to_stage(const void* h_plan, const void* d_plan,
+                                              int64_t tile_begin, int64_t tile_count,
+                                              float* stage, int64_t stage_elems,
+                                              int32_t max_workgroups, tide_stream_t stream) {
+    if (!d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    tide_status st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, stage_elems,
+                                    max_workgroups, &h);
+    if (st != TIDE_OK) return st;
+    const uint8_t* d = static_cast<const uint8_t*>(d_plan);
+    const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
+    const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
+    int R = h.R;
+    int64_t T = h.rs_tile;
+    DenseKernel k = pick_dense(R, h.flags);
+    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
+    for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
+        const RsTile* tiles = all + b;
+        int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch
+                                                                  : tile_begin + tile_count - b;
+        int64_t grid = ntiles;
+        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+        if (grid > INT_MAX) grid = INT_MAX;
+        float* out = stage + (b - tile_begin) * T;
+        void* args[] = {&tiles, &ntiles, &gptr, &out, &T, &R};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return TIDE_EHIP;
+    }
+    return TIDE_OK;
+}
+
+extern "C" tide_status tide_rs_stage_to_shards(const void* h_plan, const void* d_plan,
+                                               int64_t tile_begin, int64_t tile_count,
+                                               const float* stage, int64_t stage_elems,
+                                               int32_t max_workgroups, tide_stream_t stream) {
+    if (!d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    tide_status st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, stage_elems,
+                                    max_workgroups, &h);
+    if (st != TIDE_OK) return st;
+    const uint8_t* d = static_cast<const uint8_t*>(d_plan);
+    const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
+    const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
+    int64_t T = h.rs_tile;
+    const void* k = (h.flags & kFlagNtStores)
+                        ? reinterpret_cast<const void*>(rs_drain_kernel<true>)
+                        : reinterpret_cast<const void*>(rs_drain_kernel<false>);
+    // a drain moves 8 bytes per element where the reduction moves 2R + 4:
+    // launches of the same byte size hold (2R + 4) / 8 times the tiles
+    int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles * (2 * h.R + 4) / 8 : tile_count;
+    if (per_launch < 1) per_launch = 1;
+    for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
+        const RsTile* tiles = all + b;
+        int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch
+                                                                  : tile_begin + tile_count - b;
+        int64_t grid = ntiles;
+        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+        if (grid > INT_MAX) grid = INT_MAX;
+        const float* src = stage + (b - tile_begin) * T;
+        void* args[] = {&tiles, &ntiles, &src, &T, &obase};
+        hipError_t e = hipLaunchKernel(k, dim3((unsigned)grid), dim3(kBlock), args, 0,
+                                       reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return TIDE_EHIP;
     }
     return TIDE_OK;

@@ -19,4 +19,18 @@ namespace tide {
 tide_status check_stage(const void* h_plan, const uint64_t* h_stage, int64_t slot_stride,
                         bool* vec_ok);
 
+// Whether the byte range [lo, hi) overlaps any gradient tensor or any
+// output arena of the plan (a reduce-scatter plan).
+bool overlaps_rs_buffers(const void* h_plan, uint64_t lo, uint64_t hi);
+
+// Checks shared by the two-phase pipeline calls: a reduce-scatter plan, a
+// valid tile range, a 16-byte aligned staging chunk of at least
+// tile_count * rs_tile floats that overlaps no gradient or output arena, a
+// 16-byte aligned device plan (when d_plan is not NULL).  On success *h
+// holds the plan header.
+struct PlanHeader;
+tide_status check_pipeline(const void* h_plan, const void* d_plan, int64_t tile_begin,
+                           int64_t tile_count, const float* stage, int64_t stage_elems,
+                           int32_t max_workgroups, PlanHeader* h);
+
 }  // namespace tide

@@ -358,3 +358,39 @@ def test_staging_validation_before_touching_the_gpu():
     assert fold(good, plan=junk) == -7 and stage_dma(good, plan=junk) == -7
     assert L.tide_ag_place_dma(blob.ctypes.data, None) == -6     # no placement pointers
     assert L.tide_ag_place_dma(junk.ctypes.data, None) == -7
+
+
+def test_pipeline_phases_validate_before_touching_the_gpu():
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S)
+    L = _lib.lib()
+    blob, info = api.tide_desc_build(SHAPES, R, g, o, None, None)
+    n = int(info.rs_tiles)
+    T = int(info.rs_tile_elems)
+    fake_dev = ctypes.c_void_p(1 << 44)
+    stage = 1 << 45
+    for fn in (L.tide_rs_tiles_to_stage, L.tide_rs_stage_to_shards):
+        def call(b=0, cnt=n, st=stage, elems=n * T, mw=0, plan=blob):
+            return fn(plan.ctypes.data, fake_dev, b, cnt, ctypes.c_void_p(st) if st else None, elems,
+                      mw, None)
+        assert call(b=-1) == -1 and call(cnt=n + 1) == -1 and call(b=n, cnt=1) == -1
+        assert call(st=0) == -1                                   # no staging chunk
+        assert call(st=stage + 4) == -2                           # not 16-byte aligned
+        assert call(elems=n * T - 1) == -1                        # chunk too small
+        assert call(st=o[1]) == -3                                # over an output arena
+        assert call(st=(g[1] // 16) * 16) == -3                   # over a gradient tensor
+        assert call(mw=-1) == -1
+        ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
+        assert call(plan=ag_blob) == -6
+        assert call(plan=np.zeros(4096, np.uint8)) == -7
+        assert call(cnt=0, elems=0) == 0                          # empty range: nothing to do
+    D = L.tide_rs_stage_to_shards_sdma
+
+    def dcall(b=0, cnt=n, st=stage, elems=n * T, plan=blob):
+        return D(plan.ctypes.data, b, cnt, ctypes.c_void_p(st) if st else None, elems, None)
+    assert dcall(b=-1) == -1 and dcall(cnt=n + 1) == -1 and dcall(st=0) == -1
+    assert dcall(st=stage + 4) == -2 and dcall(elems=n * T - 1) == -1 and dcall(st=o[1]) == -3
+    assert dcall(plan=np.zeros(4096, np.uint8)) == -7 and dcall(cnt=0, elems=0) == 0
+    assert L.tide_rs_tiles_to_stage(blob.ctypes.data, None, 0, n, ctypes.c_void_p(stage), n * T, 0,
+                                    None) == -1                   # no device plan

@@ -1,0 +1,99 @@
+"""GPU parity of the two-phase pipeline emulation: phase 1 reduces chunks of
+tiles into staging chunks, phase 2 moves them into the shard arenas; run on
+two streams through a ring of staging chunks.  Bit for bit against the
+oracle and against the in-place kernel."""
+import pytest
+import torch
+
+from shard_placement_amd import api, configs, harness, pipeline
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _wl(shapes, R, key, sigma=1.0):
+    shapes = tuple(tuple(s) for s in shapes)
+    return configs.Workload(key=key, name="adhoc", R=R, names=tuple("p%d" % i for i in range(len(shapes))),
+                            shapes=shapes, sigma=sigma)
+
+
+CASES = [
+    (1, [(37, 16), (5,)]),
+    (3, [(37, 16), (64, 64), (5,), ()]),
+    (4, [(1001, 3), (0, 5), (2, 2, 2), (9,)]),
+    (8, [(8192,), (1024, 64), (6, 40)]),
+    (17, [(300, 16)]),
+    (32, [(6, 5120), (5120,)]),
+    (64, [(1001, 64), (128,), (3, 8)]),
+]
+
+
+@pytest.mark.parametrize("R,shapes", CASES, ids=[str(c[0]) for c in CASES])
+def test_phases_in_sequence_bitwise(R, shapes):
+    """Phase 1 over all tiles into one staging chunk, then phase 2."""
+    w = _wl(shapes, R, 900 + R)
+    st = harness.setup(w, with_ag=False)
+    n, T = int(st.plan.info.rs_tiles), int(st.plan.info.rs_tile_elems)
+    stage = torch.empty(max(1, n) * T, dtype=torch.float32, device="cuda")
+    gu.say("pipeline phases", R, shapes)
+    api.tide_rs_tiles_to_stage(st.plan.blob, st.plan.d_blob, 0, n, stage)
+    api.tide_rs_stage_to_shards(st.plan.blob, st.plan.d_blob, 0, n, stage)
+    torch.cuda.synchronize()
+    gu.check_rs_full(st)
+
+
+@pytest.mark.parametrize("chunk,depth,phase2", [(1, 1, "cu"), (7, 2, "cu"), (64, 3, "cu"),
+                                                (10 ** 6, 1, "cu"), (1, 2, "sdma"), (7, 2, "sdma"),
+                                                (64, 1, "sdma")])
+def test_two_streams_ring_bitwise(chunk, depth, phase2):
+    shapes = [(4096, 96), (96,), (1001, 24), (5,)]
+    R = 8
+    w = _wl(shapes, R, 950, sigma=1e-3)
+    st = harness.setup(w, with_ag=False)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    tp = pipeline.TwoPhase(st.plan, chunk, depth, phase2)
+    try:
+        gu.say("pipeline ring", chunk, depth, phase2, tp.chunks())
+        tp.run()
+        torch.cuda.synchronize()
+    finally:
+        tp.close()
+    for r in range(R):
+        assert torch.equal(st.out[r].view(torch.int32), ref[r].view(torch.int32)), r
+    gu.check_out_guards(st, 0)
+
+
+@pytest.mark.big
+@pytest.mark.parametrize("phase2", ["cu", "sdma"])
+def test_full_size_pipeline_matches_in_place(phase2):
+    w = configs.get(2)
+    st = harness.setup(w, with_ag=False, guard=0)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    tp = pipeline.TwoPhase(st.plan, int(st.plan.info.rs_launch_tiles), 2, phase2)
+    try:
+        gu.say("full-size pipeline", w.name, phase2, tp.chunks())
+        tp.run()
+        torch.cuda.synchronize()
+    finally:
+        tp.close()
+    for r in range(w.R):
+        assert torch.equal(st.out[r].view(torch.int32), ref[r].view(torch.int32)), r
+    del ref, tp
+    st.free()
+    torch.cuda.empty_cache()
