@@ -43,10 +43,14 @@
  *     round-to-nearest-even add, subnormals kept.
  *
  * Memory and ownership: the caller owns every buffer, including the plan
- * blob (host) and its device copy.  The library allocates no device memory,
- * keeps no state between calls and never synchronises a stream; launches
- * are asynchronous on the caller's stream.  A plan holds raw device
- * addresses: it is invalid once any of them is freed.
+ * blob (host) and its device copy.  The library allocates no device memory.
+ * Kernel launches are asynchronous on the caller's stream and synchronise
+ * nothing; the copy-engine calls issued through ROCr (tide_ag_place_dma,
+ * tide_rs_stage_dma) are host-synchronous instead (they wait for the
+ * caller's stream, then for their copies).  The only state kept between
+ * calls is, per device, the ROCr agent and copy-engine list those calls look
+ * up once (guarded by a mutex).  A plan holds raw device addresses: it is
+ * invalid once any of them is freed.
  *
  * Errors: every entry point returns a tide_status; nothing is thrown
  * across the ABI and no launch is made when validation fails.  Faults
