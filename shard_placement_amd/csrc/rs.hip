@@ -92,11 +92,13 @@ __device__ __forceinline__ void acc_add(float (&a)[8], u32x4 v) {
 // x+8, x+16, ... .  Regrouping so that each XCD takes runs of kXcdGroup
 // consecutive tiles keeps the tiles one XCD works on at a time (and so its
 // L2 and the DRAM rows it opens for the R source streams) on neighbouring
-// addresses; measured +5-7% at R = 16..64 and neutral at R = 8.  The tail
-// that does not fill whole groups keeps the identity mapping; a capped
-// grid (workgroups striding over tiles) is left as is.
+// addresses; measured +5-7% at R = 16..64 and neutral at R = 8 (runs of 8
+// against none), and runs of 32 another +0.5-1% over runs of 8 (runs of
+// 128: -1.5% at R = 8).  The tail that does not fill whole groups keeps the
+// identity mapping; a capped grid (workgroups striding over tiles) is left
+// as is.
 constexpr int kXcds = 8;
-constexpr int kXcdGroup = 8;
+constexpr int kXcdGroup = 32;
 
 __device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles) {
     if ((int64_t)gridDim.x != ntiles) return b;

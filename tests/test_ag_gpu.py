@@ -57,11 +57,10 @@ CASES = [
 
 
 @pytest.mark.parametrize("R,shapes", CASES, ids=[str(c[0]) for c in CASES])
-@pytest.mark.parametrize("engine", ["cu", "sdma", "dma"])
-@pytest.mark.parametrize("tile", [0, 2048])
+@pytest.mark.parametrize("engine,tile", [("cu", 0), ("cu", 2048), ("sdma", 0), ("dma", 0)])
 def test_ragged_shapes_bitwise(R, shapes, engine, tile):
-    if engine != "cu" and tile:
-        pytest.skip("the copy-engine paths have no tiles")
+    """tile: the placement tile size of the compute-unit path (0: default);
+    the copy-engine paths have no tiles."""
     w = _wl(shapes, R, key=310 + R)
     gu.say("ragged ag", R, shapes, engine, tile)
     st = harness.setup(w, with_rs=False, ag_tile=tile)

@@ -71,13 +71,15 @@ def test_ragged_shapes_bitwise(R, shapes, tile, order):
     gu.check_rs_full(st, order)
 
 
-@pytest.mark.parametrize("R,shapes", RANDOM_CASES[::3], ids=[str(c[0]) for c in RANDOM_CASES[::3]])
-@pytest.mark.parametrize("slot_reuse", [False, True])
+SEPARATE_CASES = [(R, shapes, reuse) for R, shapes in RANDOM_CASES[::3] for reuse in (False, True)
+                  if R >= 2 or not reuse]  # Slot-Reuse needs R >= 2
+
+
+@pytest.mark.parametrize("R,shapes,slot_reuse", SEPARATE_CASES,
+                         ids=["%d-%s" % (c[0], "reuse" if c[2] else "own") for c in SEPARATE_CASES])
 def test_rank_arenas_allocated_separately(R, shapes, slot_reuse):
     """Every rank's gradient and output arena in an allocation of its own
     (the packed rows are the default): same bits."""
-    if slot_reuse and R < 2:
-        pytest.skip("Slot-Reuse needs R >= 2")
     w = _wl(shapes, R, key=100 + R)
     gu.say("separate arenas R", R, shapes, slot_reuse)
     st = harness.setup(w, with_ag=False, rank_layout="separate", slot_reuse=slot_reuse)
