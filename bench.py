@@ -32,8 +32,12 @@ sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 PROFILES = os.path.join(HERE, "profiles")
-RS_SOURCES = ["shard_placement_amd/csrc/rs.hip", "shard_placement_amd/csrc/plan_format.h"]
-AG_SOURCES = ["shard_placement_amd/csrc/ag.hip", "shard_placement_amd/csrc/plan_format.h"]
+# what decides a kernel's launches: its source, the shared headers, and the
+# plan builder (tile sizes, order, kinds)
+RS_SOURCES = ["shard_placement_amd/csrc/rs.hip", "shard_placement_amd/csrc/plan_format.h",
+              "shard_placement_amd/csrc/xcd_map.h", "shard_placement_amd/csrc/plan.cpp"]
+AG_SOURCES = ["shard_placement_amd/csrc/ag.hip", "shard_placement_amd/csrc/plan_format.h",
+              "shard_placement_amd/csrc/xcd_map.h", "shard_placement_amd/csrc/plan.cpp"]
 
 
 def log(*a):

@@ -11,7 +11,8 @@
 //
 // Two engines do it:
 //   tide_ag_place       a compute kernel: one short-lived workgroup per tile
-//                       of up to ag_tile elements; 16-byte loads and stores
+//                       of up to ag_tile elements (runs of consecutive tiles
+//                       per XCD, as in the reduce-scatter); 16-byte loads and stores
 //                       where both ends allow it (4 vectors in flight per
 //                       lane), 4-byte or 2-byte moves otherwise.
 //   tide_ag_place_sdma  host-issued copies.  engine_only = 1: one 1-D copy
@@ -31,6 +32,7 @@
 
 #include "plan_format.h"
 #include "tide.h"
+#include "xcd_map.h"
 
 using namespace tide;
 
@@ -176,8 +178,8 @@ __global__ __launch_bounds__(kBlock) void ag_kernel(const AgTile* __restrict__ t
                                                     int64_t ntiles,
                                                     const uint16_t* __restrict__ gathered,
                                                     const uint64_t* __restrict__ full) {
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const AgTile tile = tiles[t];
+    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const AgTile tile = tiles[tile_of(b, ntiles)];
         const uint16_t* src = gathered + tile.src;
         uint16_t* dst = reinterpret_cast<uint16_t*>(full[tile.p]) + tile.dst;
         if (tile.kind == kAgVec16)

@@ -372,20 +372,31 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     std::vector<AgTile> ag;
     if (has_rs) {
         rs.reserve((size_t)std::min<int64_t>(rs_tiles_bound(ps, R, o.rs_tile), (int64_t)1 << 24));
+        // per param: whether every rank's source shares one 16-byte phase
+        // (the vector path), and the first 16-byte aligned flat index
+        std::vector<char> vec_ok(P, 0);
+        std::vector<int64_t> phase(P, 0);
         for (int32_t p = 0; p < P; ++p) {
-            const ParamDesc& d = ps[p];
-            if (d.m == 0) continue;
-            // every rank's source must share one 16-byte phase for the vector path
-            bool vec_ok = true;
-            uint64_t a0 = (uint64_t)(uintptr_t)grads[p];
-            for (int32_t q = 1; q < R && vec_ok; ++q)
-                if (((uint64_t)(uintptr_t)grads[(int64_t)q * P + p]) % 16 != a0 % 16) vec_ok = false;
-            if (d.n == 0) vec_ok = false;
-            // j is 16-byte aligned when (a0 + 2j) % 16 == 0
-            int64_t phase = (int64_t)(((16 - a0 % 16) % 16) / 2);
-            for (int32_t r = 0; r < R; ++r) {
+            bool ok = ps[p].n > 0;
+            const uint64_t a0 = (uint64_t)(uintptr_t)grads[p];
+            for (int32_t q = 1; q < R && ok; ++q)
+                if (((uint64_t)(uintptr_t)grads[(int64_t)q * P + p]) % 16 != a0 % 16) ok = false;
+            vec_ok[p] = ok;
+            phase[p] = (int64_t)(((16 - a0 % 16) % 16) / 2);  // (a0 + 2j) % 16 == 0
+        }
+        // Output-stationary order: rank outer, then param, then index, so
+        // that each rank's fp32 arena is written front to back, one output
+        // stream at a time.  Measured against param-outer order (every
+        // rank's shard of a param in turn), same bits: +8% on a layer of
+        // 389 params at R = 16 (whose shards of ~100 K elements otherwise
+        // keep all 16 arenas open for writing at once), +1% at R = 32,
+        // neutral at R = 8 and 64.
+        for (int32_t r = 0; r < R; ++r) {
+            for (int32_t p = 0; p < P; ++p) {
+                const ParamDesc& d = ps[p];
+                if (d.m == 0) continue;
                 int64_t jb = (int64_t)r * d.m, je = std::min<int64_t>(d.n, jb + d.m);
-                if (jb < je) cut_rs_run(rs, p, r, jb, je, d.off, vec_ok, phase, o.rs_tile);
+                if (jb < je) cut_rs_run(rs, p, r, jb, je, d.off, vec_ok[p] != 0, phase[p], o.rs_tile);
                 int64_t pb = std::max<int64_t>(d.n, jb), pe = jb + d.m;
                 for (int64_t x = pb; x < pe; x += o.rs_tile) {
                     RsTile t;

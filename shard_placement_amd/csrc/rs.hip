@@ -10,7 +10,7 @@
 //
 // Work decomposition: the host plan cuts every (param, rank) shard into
 // tiles (plan.cpp); one short-lived 256-lane workgroup takes one tile (or
-// strides over tiles when the grid is capped), runs of 8 consecutive tiles
+// strides over tiles when the grid is capped), runs of 32 consecutive tiles
 // going to one XCD.  A call is cut into launches of about 256 MiB of
 // traffic (the plan's launch size) so that kernels on other queues get
 // whole compute units at the launch boundaries.  In a vector tile each lane
@@ -30,6 +30,7 @@
 #include "plan_format.h"
 #include "stage_check.h"
 #include "tide.h"
+#include "xcd_map.h"
 
 using namespace tide;
 
@@ -87,27 +88,8 @@ __device__ __forceinline__ void acc_add(float (&a)[8], u32x4 v) {
     a[6] = a[6] + bf_lo(v.w); a[7] = a[7] + bf_hi(v.w);
 }
 
-// Workgroup -> tile.  The dispatcher hands consecutive workgroup IDs to the
-// 8 XCDs in turn; with one workgroup per tile, XCD x would get tiles x,
-// x+8, x+16, ... .  Regrouping so that each XCD takes runs of kXcdGroup
-// consecutive tiles keeps the tiles one XCD works on at a time (and so its
-// L2 and the DRAM rows it opens for the R source streams) on neighbouring
-// addresses; measured +5-7% at R = 16..64 and neutral at R = 8 (runs of 8
-// against none), and runs of 32 another +0.5-1% over runs of 8 (runs of
-// 128: -1.5% at R = 8).  The tail that does not fill whole groups keeps the
-// identity mapping; a capped grid (workgroups striding over tiles) is left
-// as is.
-constexpr int kXcds = 8;
-constexpr int kXcdGroup = 32;
 
-__device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles) {
-    if ((int64_t)gridDim.x != ntiles) return b;
-    constexpr int64_t span = (int64_t)kXcds * kXcdGroup;
-    const int64_t full = (ntiles / span) * span;
-    if (b >= full) return b;
-    const int64_t x = b % kXcds, i = b / kXcds;
-    return (i / kXcdGroup) * span + x * kXcdGroup + (i % kXcdGroup);
-}
+
 
 // The compute unit a workgroup runs on, for the optional census: the HW_ID
 // hardware register's cu_id [11:8], sh_id [12] and se_id [15:13] fields
