@@ -204,16 +204,28 @@ def pipeline_leg(st, fused_ms: float) -> dict:
     t1 = ev_time(lambda: api.tide_rs_tiles_to_stage(plan.blob, plan.d_blob, 0, n, full))
     t2 = {"cu": ev_time(lambda: api.tide_rs_stage_to_shards(plan.blob, plan.d_blob, 0, n, full)),
           "sdma": ev_time(lambda: api.tide_rs_stage_to_shards_sdma(plan.blob, 0, n, full), reps=1)}
+    # phase 2 confined to a few CUs: a consumer with a link's bandwidth
+    link_cus = 8
+    s8 = api.tide_stream_create_cu_limited(link_cus)
+    try:
+        with torch.cuda.stream(s8):
+            t2["cu%d" % link_cus] = ev_time(
+                lambda: api.tide_rs_stage_to_shards(plan.blob, plan.d_blob, 0, n, full, stream=s8),
+                reps=1)
+    finally:
+        torch.cuda.synchronize()
+        api.tide_stream_destroy(s8)
     del full
     torch.cuda.empty_cache()
     runs = []
     same = True
-    for phase2 in ("cu", "sdma"):
+    for phase2 in ("cu", "sdma", "cu%d" % link_cus):
         for mult, depth in ((0.25, 2), (1, 1), (1, 2), (1, 4), (4, 2)):
             chunk = max(1, int(L * mult))
-            tp = pipeline.TwoPhase(plan, chunk, depth, phase2)
+            tp = pipeline.TwoPhase(plan, chunk, depth, "sdma" if phase2 == "sdma" else "cu",
+                                   link_cus if phase2 != "cu" and phase2 != "sdma" else 0)
             try:
-                t = ev_time(tp.run, reps=1 if phase2 == "sdma" else 2)
+                t = ev_time(tp.run, reps=1 if phase2 != "cu" else 2)
             finally:
                 tp.close()
             same = same and all(torch.equal(o[: st.S].view(torch.int32), r.view(torch.int32))
@@ -226,7 +238,8 @@ def pipeline_leg(st, fused_ms: float) -> dict:
     del ref
     torch.cuda.empty_cache()
     return {"phase1_ms": round(t1, 4), "phase2_cu_ms": round(t2["cu"], 4),
-            "phase2_sdma_ms": round(t2["sdma"], 3), "fused_ms": round(fused_ms, 4),
+            "phase2_sdma_ms": round(t2["sdma"], 3),
+            "phase2_cu%d_ms" % link_cus: round(t2["cu%d" % link_cus], 3), "fused_ms": round(fused_ms, 4),
             "layer_staging_mib": round(n * T * 4 / 2 ** 20, 1), "runs": runs,
             "same_bits_as_fused": bool(same),
             "overlap_def": "(phase1 alone + phase2 alone - pipelined) / min(phase1, phase2)"}

@@ -22,11 +22,13 @@ from . import api
 
 
 class TwoPhase:
-    """phase2: "cu" moves each chunk with a kernel at HBM speed; "sdma"
-    moves it with stream-ordered copy-engine copies, whose bandwidth (tens
-    of GB/s per engine) is closer to a network link's."""
+    """phase2: "cu" moves each chunk with a kernel; "sdma" with
+    stream-ordered copy-engine copies.  phase2_cus confines the phase-2
+    kernel to that many compute units (0: all), which caps its bandwidth
+    the way a network link would."""
 
-    def __init__(self, plan: "api.Plan", chunk_tiles: int, depth: int = 2, phase2: str = "cu"):
+    def __init__(self, plan: "api.Plan", chunk_tiles: int, depth: int = 2, phase2: str = "cu",
+                 phase2_cus: int = 0):
         if chunk_tiles < 1 or depth < 1:
             raise ValueError("chunk_tiles and depth must be >= 1")
         if phase2 not in ("cu", "sdma"):
@@ -43,7 +45,7 @@ class TwoPhase:
         # two streams with hardware queues of their own (streams that share a
         # queue run one after the other)
         self.s1 = api.tide_stream_create_cu_limited(n_cu)
-        self.s2 = api.tide_stream_create_cu_limited(n_cu)
+        self.s2 = api.tide_stream_create_cu_limited(phase2_cus or n_cu)
 
     @property
     def staging_bytes(self) -> int:
