@@ -50,10 +50,11 @@ def test_phases_in_sequence_bitwise(R, shapes):
     gu.check_rs_full(st)
 
 
-@pytest.mark.parametrize("chunk,depth,phase2", [(1, 1, "cu"), (7, 2, "cu"), (64, 3, "cu"),
-                                                (10 ** 6, 1, "cu"), (1, 2, "sdma"), (7, 2, "sdma"),
-                                                (64, 1, "sdma")])
-def test_two_streams_ring_bitwise(chunk, depth, phase2):
+@pytest.mark.parametrize("chunk,depth,phase2,cus", [(1, 1, "cu", 0), (7, 2, "cu", 0), (64, 3, "cu", 0),
+                                                    (10 ** 6, 1, "cu", 0), (7, 2, "cu", 8),
+                                                    (1, 2, "sdma", 0), (7, 2, "sdma", 0),
+                                                    (64, 1, "sdma", 0)])
+def test_two_streams_ring_bitwise(chunk, depth, phase2, cus):
     shapes = [(4096, 96), (96,), (1001, 24), (5,)]
     R = 8
     w = _wl(shapes, R, 950, sigma=1e-3)
@@ -63,9 +64,9 @@ def test_two_streams_ring_bitwise(chunk, depth, phase2):
     ref = [o.clone() for o in st.out]
     for o in st.out:
         o.view(torch.int32).fill_(-1)
-    tp = pipeline.TwoPhase(st.plan, chunk, depth, phase2)
+    tp = pipeline.TwoPhase(st.plan, chunk, depth, phase2, cus)
     try:
-        gu.say("pipeline ring", chunk, depth, phase2, tp.chunks())
+        gu.say("pipeline ring", chunk, depth, phase2, cus, tp.chunks())
         tp.run()
         torch.cuda.synchronize()
     finally:
