@@ -528,6 +528,8 @@ def main():
                       ("one launch", one, 0, 0),
                       ("one launch, grid 256", one, 256, 0),
                       ("one launch, CU mask 32", one, 0, 32)]
+            # the default launches confined to part of the chip
+            modes += [("default launches, CU mask %d" % n, st.plan, 0, n) for n in (128, 64, 32, 16)]
         probe = probe_mod.run(modes, rsb, iters=40 if args.probe else 30)
         for m in probe["modes"]:
             log("probe", m)
