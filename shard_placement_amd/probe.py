@@ -45,7 +45,9 @@ def _gemm_train(a, b, c, stream, n):
 
 def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N: int = 4096,
         K: int = 8192) -> Dict:
-    """Time the GEMM alone, then beside each mode's reduce-scatter.  The
+    """Time the GEMM alone, then, per mode, alone again and beside the
+    mode's reduce-scatter (the slowdown is against the mode's own alone
+    time).  The
     reduce-scatter always runs on a CU-masked stream, which HIP backs with a
     hardware queue of its own (with the full mask when the mode has none):
     two streams that share a hardware queue run one after the other, which
@@ -76,8 +78,13 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
             e1.record(rs_stream)
             torch.cuda.synchronize()
             rs_alone = e0.elapsed_time(e1) / 3
+            # the GEMM alone again, right before this mode (clocks drift
+            # over a sweep; each mode is compared with its own baseline)
+            own = _gemm_train(a, b, c, gemm_stream, iters)
+            torch.cuda.synchronize()
+            t0m = _median([e0.elapsed_time(e1) for e0, e1 in own])
             # concurrent: enough reduce-scatters to cover the GEMM train twice
-            n_rs = max(2, int(2.0 * iters * t0 / rs_alone) + 2)
+            n_rs = max(2, int(2.0 * iters * t0m / rs_alone) + 2)
             r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             r0.record(rs_stream)
             for _ in range(n_rs):
@@ -99,10 +106,11 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
                 "rs_alone_ms": round(rs_alone, 4),
                 "rs_alone_gbps": round(rs_bytes / (rs_alone * 1e-3) / 1e9, 1),
                 "rs_concurrent_gbps": round(rs_bytes / (rs_conc * 1e-3) / 1e9, 1),
+                "t_gemm_alone_ms": round(t0m, 4),
                 "t_gemm_concurrent_ms": round(t1, 4) if t1 else None,
                 "gemm_inside": len(inside),
                 # no GEMM inside the window: it waited for the whole train
-                "gemm_slowdown_pct": round(100.0 * (t1 / t0 - 1.0), 2) if t1 else "starved",
+                "gemm_slowdown_pct": round(100.0 * (t1 / t0m - 1.0), 2) if t1 else "starved",
             })
         finally:
             torch.cuda.synchronize()
