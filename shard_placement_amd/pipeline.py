@@ -86,6 +86,16 @@ class TwoPhase:
         cur.wait_stream(self.s2)
 
     def close(self) -> None:
+        """Wait for the device and release the two streams (idempotent)."""
+        if self.s1 is None:
+            return
         torch.cuda.synchronize()
         api.tide_stream_destroy(self.s1)
         api.tide_stream_destroy(self.s2)
+        self.s1 = self.s2 = None
+
+    def __enter__(self) -> "TwoPhase":
+        return self
+
+    def __exit__(self, *exc) -> None:
+        self.close()
