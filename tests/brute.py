@@ -28,10 +28,40 @@ def rs_brute(shapes, R, grads_bits):
                 for col in range(c):
                     if row < d0:
                         acc = _f32(grads_bits[0][p][row * c + col])
-                        for q in range(1, R):
-                            acc = np.float32(acc + _f32(grads_bits[q][p][row * c + col]))
+                        with np.errstate(over="ignore"):  # IEEE overflow to inf is the result
+                            for q in range(1, R):
+                                acc = np.float32(acc + _f32(grads_bits[q][p][row * c + col]))
                         shard.append(acc)
                     else:
                         shard.append(np.float32(0.0))
             out[(r, p)] = shard
+    return out
+
+
+def ag_brute(shapes, R, gathered_bits):
+    """All-gather placement by rows: returns P lists of uint16 (d0*c each):
+    row i of param p comes from slot i // s, row i % s of that slot's shard
+    of p."""
+    d0s, cs = [], []
+    for shp in shapes:
+        d0s.append(shp[0] if len(shp) else 1)
+        c = 1
+        for d in shp[1:]:
+            c *= d
+        cs.append(c)
+    ms = [(-(-d0 // R)) * c for d0, c in zip(d0s, cs)]
+    offs, S = [], 0
+    for m in ms:
+        offs.append(S)
+        S += m
+    out = []
+    for p in range(len(shapes)):
+        d0, c = d0s[p], cs[p]
+        s = -(-d0 // R)
+        full = []
+        for row in range(d0):
+            r, i = divmod(row, s)
+            base = r * S + offs[p] + i * c
+            full.extend(int(gathered_bits[base + k]) for k in range(c))
+        out.append(full)
     return out
