@@ -438,6 +438,20 @@ def main():
     log("step %.3f ms; RS avg %.3f ms (min %.3f) = %.0f GB/s; AG avg %.3f ms = %.0f GB/s" % (
         ms_step, rs_avg, min(rs_ms), rs_gbs, ag_avg, ag_gbs))
 
+    # the optional pairwise (tree) rank order, same tiles and launches
+    st.plan.rs(order="tree")
+    torch.cuda.synchronize()
+    te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    te0.record()
+    for _ in range(3):
+        st.plan.rs(order="tree")
+    te1.record()
+    torch.cuda.synchronize()
+    tree_ms = te0.elapsed_time(te1) / 3
+    st.plan.rs()  # leave the fixed-order shards in place for the checks below
+    torch.cuda.synchronize()
+    log("RS tree order: %.3f ms = %.0f GB/s" % (tree_ms, rsb / (tree_ms * 1e-3) / 1e9))
+
     # the same step captured once in a HIP graph and replayed (launch-bound
     # host work removed; the device work is identical)
     graph_ms = None
@@ -523,14 +537,15 @@ def main():
                   st.plan, 0, 0)]
         if args.probe:
             one = plan_with(-1)
-            modes += [("128 MiB launches", plan_with(128), 0, 0),
+            modes += [("256 MiB launches", plan_with(256), 0, 0),
+                      ("128 MiB launches", plan_with(128), 0, 0),
                       ("64 MiB launches", plan_with(64), 0, 0),
                       ("one launch", one, 0, 0),
                       ("one launch, grid 256", one, 256, 0),
                       ("one launch, CU mask 32", one, 0, 32)]
             # the default launches confined to part of the chip
             modes += [("default launches, CU mask %d" % n, st.plan, 0, n) for n in (128, 64, 32, 16)]
-        probe = probe_mod.run(modes, rsb, iters=40 if args.probe else 30)
+        probe = probe_mod.run(modes, rsb, iters=40)
         for m in probe["modes"]:
             log("probe", m)
 
@@ -565,6 +580,7 @@ def main():
         "rs_gbps": round(rs_gbs, 1),
         "rs_frac_hbm": round(rs_gbs / HBM_PEAK_GBS, 4),
         "rs_ms": round(rs_avg, 4),
+        "rs_tree_gbps": round(rsb / (tree_ms * 1e-3) / 1e9, 1),
         "ag_gbps": round(ag_gbs, 1),
         "ag_frac_hbm": round(ag_gbs / HBM_PEAK_GBS, 4),
         "ag_ms": round(ag_avg, 4),

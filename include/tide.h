@@ -99,7 +99,9 @@ typedef struct tide_opts {
     int32_t launch_mib;    /* algorithmic MiB moved per kernel launch: a call is cut
                               into launches of about this size, so that concurrent
                               kernels on other streams get whole compute units at
-                              the launch boundaries (0: default 256; -1: one launch) */
+                              the launch boundaries (0: defaults, 160 MiB and at
+                              least 1024 tiles for the reduce-scatter, 256 MiB for
+                              the placement; -1: one launch) */
 } tide_opts;
 
 /* Access hints (results are identical with any combination). */

@@ -41,19 +41,28 @@ int32_t default_rs_tile(int32_t R) {
 constexpr int32_t kDefaultAgTile = 2048;
 constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 
-// Launch granularity: about 256 MiB of algorithmic traffic per kernel
-// launch.  Measured on MI355X next to a single-wave bf16 GEMM on another
-// hardware queue: one launch for a whole layer starves the GEMM (it waits
-// for free compute units that the stream of short workgroups never leaves);
-// launch boundaries every 64-256 MiB let it in with <5% slowdown, for 2-4%
-// less reduce-scatter bandwidth alone.
-constexpr int32_t kDefaultLaunchMiB = 256;
+// Launch granularity.  Measured on MI355X next to a single-wave bf16 GEMM
+// on another hardware queue: one launch for a whole layer starves the GEMM
+// (it waits for free compute units that the stream of short workgroups
+// never leaves); with launch boundaries the GEMM waits about half a launch.
+// Reduce-scatter: about 160 MiB of algorithmic traffic per launch (against
+// 256 MiB it halves the slowdown, +3..6% vs +9..13%, for 1-3% less
+// bandwidth; 128 MiB costs another 3%), but at least 1024 tiles (4
+// workgroups per CU: at R = 64 a 160 MiB launch holds only 620 tiles and
+// loses 7%).  Placement: 256 MiB (its own interference is not what the
+// probe measures, and shorter launches cost it 4%).  An explicit launch
+// size applies to both.
+constexpr int32_t kDefaultRsLaunchMiB = 160;
+constexpr int64_t kMinRsLaunchTiles = 1024;
+constexpr int32_t kDefaultAgLaunchMiB = 256;
 
 struct Resolved {
     int64_t align;
     int32_t rs_tile, ag_tile;
     uint32_t flags;
-    int64_t launch_bytes;  // <= 0: unlimited
+    int64_t rs_launch_bytes;  // <= 0: unlimited
+    int64_t ag_launch_bytes;
+    int64_t rs_min_tiles;     // lower bound on tiles per reduce-scatter launch
 };
 
 tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
@@ -61,11 +70,16 @@ tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
     out->rs_tile = default_rs_tile(R);
     out->ag_tile = kDefaultAgTile;
     out->flags = kDefaultFlags;
-    out->launch_bytes = (int64_t)kDefaultLaunchMiB << 20;
+    out->rs_launch_bytes = (int64_t)kDefaultRsLaunchMiB << 20;
+    out->ag_launch_bytes = (int64_t)kDefaultAgLaunchMiB << 20;
+    out->rs_min_tiles = kMinRsLaunchTiles;
     if (!o) return TIDE_OK;
     if (o->launch_mib < -1 || o->launch_mib > (1 << 20)) return TIDE_EINVAL;
-    if (o->launch_mib == -1) out->launch_bytes = 0;
-    if (o->launch_mib > 0) out->launch_bytes = (int64_t)o->launch_mib << 20;
+    if (o->launch_mib != 0) {
+        out->rs_launch_bytes = out->ag_launch_bytes =
+            o->launch_mib == -1 ? 0 : (int64_t)o->launch_mib << 20;
+        out->rs_min_tiles = 1;
+    }
     if (o->align_elems < 1 || o->align_elems > (int64_t)1 << 20) return TIDE_EINVAL;
     out->align = o->align_elems;
     if (o->rs_tile_elems != 0) {
@@ -430,10 +444,10 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     const int64_t ag_tile_bytes = (int64_t)o.ag_tile * 4;
     int64_t rs_launch = std::max<int64_t>(1, (int64_t)rs.size());
     int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
-    if (o.launch_bytes > 0) {
-        rs_launch = std::min(rs_launch, std::max<int64_t>(1, o.launch_bytes / rs_tile_bytes));
-        ag_launch = std::min(ag_launch, std::max<int64_t>(1, o.launch_bytes / ag_tile_bytes));
-    }
+    if (o.rs_launch_bytes > 0)
+        rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, o.rs_launch_bytes / rs_tile_bytes));
+    if (o.ag_launch_bytes > 0)
+        ag_launch = std::min(ag_launch, std::max<int64_t>(1, o.ag_launch_bytes / ag_tile_bytes));
     if (info) {
         std::memset(info, 0, sizeof(*info));
         info->R = R;

@@ -11,7 +11,7 @@
 // Work decomposition: the host plan cuts every (param, rank) shard into
 // tiles (plan.cpp); one short-lived 256-lane workgroup takes one tile (or
 // strides over tiles when the grid is capped), runs of 32 consecutive tiles
-// going to one XCD.  A call is cut into launches of about 256 MiB of
+// going to one XCD.  A call is cut into launches of about 160 MiB of
 // traffic (the plan's launch size) so that kernels on other queues get
 // whole compute units at the launch boundaries.  In a vector tile each lane
 // owns 8 consecutive elements: it issues one 16-byte load per rank (a batch
@@ -209,11 +209,13 @@ __device__ __forceinline__ void rs_vec_fixed(const Src& src, int R, int len,
         {
             u32x4 v[U][RB];
             const int nb = EXACT ? RB : (R < RB ? R : RB);
+            // every load of the batch is issued (a rank past R re-reads rank
+            // 0, never used): guarded loads would be issued one at a time
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int b = 0; b < RB; ++b)
-                    if (EXACT || b < nb) v[u][b] = load16<NTL>(src.vec(b, e[u]));
+                    v[u][b] = load16<NTL>(src.vec((EXACT || b < nb) ? b : 0, e[u]));
             // keep the whole batch of loads in flight before any add
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -231,7 +233,7 @@ __device__ __forceinline__ void rs_vec_fixed(const Src& src, int R, int len,
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int b = 0; b < RB; ++b)
-                    if (EXACT || b < nb) v[u][b] = load16<NTL>(src.vec(q0 + b, e[u]));
+                    v[u][b] = load16<NTL>(src.vec((EXACT || b < nb) ? q0 + b : q0, e[u]));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -339,9 +341,11 @@ __device__ __forceinline__ void rs_vec_tree(const Src& src, int R, int len,
         for (int q0 = 0; q0 < R; q0 += RB) {
             u32x4 v[RB];
             const int nb = (R - q0) < RB ? (R - q0) : RB;
+            // the whole batch of loads in flight (a rank past R re-reads
+            // rank q0, never used), then the pushes
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
-                if (b < nb) v[b] = load16<NTL>(src.vec(q0 + b, e));
+            for (int b = 0; b < RB; ++b) v[b] = load16<NTL>(src.vec(b < nb ? q0 + b : q0, e));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int b = 0; b < RB; ++b)
                 if (b < nb) {
@@ -544,15 +548,23 @@ RsKernel pick_nt(uint32_t flags) {
 }
 
 // Rank batching: small power-of-two R loads every rank at once (with U
-// chunks per lane when R < 8, so that at least 8 loads are in flight); R a
-// multiple of 8 loads 8 ranks per batch; anything else batches 8 with a
-// guard.  Measured on MI355X: a second chunk per lane at R = 8 did not help
+// chunks per lane when R < 8 and the tile holds them, so that up to 8 loads
+// are in flight); R a multiple of 8 loads 8 ranks per batch; anything else
+// batches 8, the last batch re-reading a rank in place of the missing ones.  Measured on MI355X: a second chunk per lane at R = 8 did not help
 // (5.6 vs 5.8 TB/s); batches of 8 beat batches of 16 at R = 16..64 by 1-3%.
-RsKernel pick_fixed(int R, uint32_t flags) {
+// Chunks per lane for R < 8: as many as the tile holds, up to 4 (a chunk
+// past the tile end would only re-read its start).
+template <typename K, K (*PICK1)(uint32_t), K (*PICK2)(uint32_t), K (*PICK4)(uint32_t)>
+K by_chunks(int32_t tile, uint32_t flags) {
+    const int32_t chunks = tile / kTileQuantum;
+    return chunks >= 4 ? PICK4(flags) : chunks >= 2 ? PICK2(flags) : PICK1(flags);
+}
+
+RsKernel pick_fixed(int R, uint32_t flags, int32_t tile) {
     switch (R) {
-        case 1: return pick_nt<1, true, 4>(flags);
-        case 2: return pick_nt<2, true, 4>(flags);
-        case 4: return pick_nt<4, true, 4>(flags);
+        case 1: return by_chunks<RsKernel, pick_nt<1, true, 1>, pick_nt<1, true, 2>, pick_nt<1, true, 4>>(tile, flags);
+        case 2: return by_chunks<RsKernel, pick_nt<2, true, 1>, pick_nt<2, true, 2>, pick_nt<2, true, 4>>(tile, flags);
+        case 4: return by_chunks<RsKernel, pick_nt<4, true, 1>, pick_nt<4, true, 2>, pick_nt<4, true, 4>>(tile, flags);
         case 8: return pick_nt<8, true, 1>(flags);
         default: break;
     }
@@ -587,11 +599,11 @@ DenseKernel pick_dense_nt(uint32_t flags) {
     return rs_dense_kernel<RB, EXACT, U, false, false>;
 }
 
-DenseKernel pick_dense(int R, uint32_t flags) {
+DenseKernel pick_dense(int R, uint32_t flags, int32_t tile) {
     switch (R) {
-        case 1: return pick_dense_nt<1, true, 4>(flags);
-        case 2: return pick_dense_nt<2, true, 4>(flags);
-        case 4: return pick_dense_nt<4, true, 4>(flags);
+        case 1: return by_chunks<DenseKernel, pick_dense_nt<1, true, 1>, pick_dense_nt<1, true, 2>, pick_dense_nt<1, true, 4>>(tile, flags);
+        case 2: return by_chunks<DenseKernel, pick_dense_nt<2, true, 1>, pick_dense_nt<2, true, 2>, pick_dense_nt<2, true, 4>>(tile, flags);
+        case 4: return by_chunks<DenseKernel, pick_dense_nt<4, true, 1>, pick_dense_nt<4, true, 2>, pick_dense_nt<4, true, 4>>(tile, flags);
         default: break;
     }
     if (R % 8 == 0) return pick_dense_nt<8, true, 1>(flags);
@@ -611,11 +623,11 @@ FoldKernel pick_fold_nt(uint32_t flags) {
 }
 
 // Same rank batching as the in-place kernels.
-FoldKernel pick_fold(int R, uint32_t flags) {
+FoldKernel pick_fold(int R, uint32_t flags, int32_t tile) {
     switch (R) {
-        case 1: return pick_fold_nt<1, true, 4>(flags);
-        case 2: return pick_fold_nt<2, true, 4>(flags);
-        case 4: return pick_fold_nt<4, true, 4>(flags);
+        case 1: return by_chunks<FoldKernel, pick_fold_nt<1, true, 1>, pick_fold_nt<1, true, 2>, pick_fold_nt<1, true, 4>>(tile, flags);
+        case 2: return by_chunks<FoldKernel, pick_fold_nt<2, true, 1>, pick_fold_nt<2, true, 2>, pick_fold_nt<2, true, 4>>(tile, flags);
+        case 4: return by_chunks<FoldKernel, pick_fold_nt<4, true, 1>, pick_fold_nt<4, true, 2>, pick_fold_nt<4, true, 4>>(tile, flags);
         default: break;
     }
     if (R % 8 == 0) return pick_fold_nt<8, true, 1>(flags);
@@ -663,7 +675,7 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
     int R = h.R;
-    RsKernel k = order == 0 ? pick_fixed(R, h.flags) : pick_tree(R, h.flags);
+    RsKernel k = order == 0 ? pick_fixed(R, h.flags, h.rs_tile) : pick_tree(R, h.flags);
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
 
     // One launch per run of per_launch tiles: the launch boundaries are where
@@ -722,7 +734,7 @@ extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_pla
     int R = h.R;
     int vec = vec_ok ? 1 : 0;
     int64_t stride = 2 * slot_stride;
-    FoldKernel k = order == 0 ? pick_fold(R, h.flags) : pick_fold_tree(R, h.flags);
+    FoldKernel k = order == 0 ? pick_fold(R, h.flags, h.rs_tile) : pick_fold_tree(R, h.flags);
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : h.n_rs_tiles;
     for (int64_t b = 0; b < h.n_rs_tiles; b += per_launch) {
         const RsTile* tiles = all + b;
@@ -752,7 +764,7 @@ extern "C" tide_status tide_rs_tiles_to_stage(const void* h_plan, const void* d_
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     int R = h.R;
     int64_t T = h.rs_tile;
-    DenseKernel k = pick_dense(R, h.flags);
+    DenseKernel k = pick_dense(R, h.flags, h.rs_tile);
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
     for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
         const RsTile* tiles = all + b;

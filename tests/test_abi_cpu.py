@@ -289,8 +289,21 @@ def test_launch_granularity():
     g, o, ga, f = _fake_ptrs(shapes, R, S)
     _, info = api.tide_desc_build(shapes, R, g, o, ga, f)
     per_tile = info.rs_tile_elems * (2 * R + 4)
-    assert info.rs_launch_tiles == min(info.rs_tiles, (256 << 20) // per_tile)
+    # library defaults: 160 MiB (at least 1024 tiles) for the reduce-scatter,
+    # 256 MiB for the placement
+    assert info.rs_launch_tiles == min(info.rs_tiles, max(1024, (160 << 20) // per_tile))
     assert info.ag_launch_tiles == min(info.ag_tiles, (256 << 20) // (info.ag_tile_elems * 4))
+    _, big = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=256)
+    assert big.rs_launch_tiles == min(big.rs_tiles, (256 << 20) // per_tile)
+    assert big.ag_launch_tiles == min(big.ag_tiles, (256 << 20) // (big.ag_tile_elems * 4))
+    # at R = 64 a 160 MiB launch would hold ~620 tiles: the floor of 1024 applies
+    R64 = 64
+    shapes64 = [(8192, 8192)]
+    _, _, _, S64 = api.tide_desc_geometry(shapes64, R64)
+    g64, o64, _, _ = _fake_ptrs(shapes64, R64, S64)
+    _, i64 = api.tide_desc_build(shapes64, R64, g64, o64, None, None)
+    assert (160 << 20) // (i64.rs_tile_elems * (2 * R64 + 4)) < 1024
+    assert i64.rs_launch_tiles == min(i64.rs_tiles, 1024)
     _, one = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=-1)
     assert one.rs_launch_tiles == one.rs_tiles and one.ag_launch_tiles == one.ag_tiles
     _, small = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=1)
