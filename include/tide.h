@@ -166,6 +166,13 @@ tide_status tide_desc_build(const tide_shape *shapes, int32_t P, int32_t R,
 /* Read back what a host plan blob holds. */
 tide_status tide_plan_query(const void *h_plan, tide_plan_info *info);
 
+/* The reduce-scatter tiles of output rank r: the plan lists tiles rank by
+ * rank (then param, then index), so they are one range [*tile_begin,
+ * *tile_begin + *tile_count) for tide_rs_bf16_to_fp32_tiles -- what one GPU
+ * of a real job would run for its own shard.  r in [0, R). */
+tide_status tide_plan_rank_tiles(const void *h_plan, int32_t r, int64_t *tile_begin,
+                                 int64_t *tile_count);
+
 /* Fused reduce-scatter [Abstract: TIDE-RS; Root: each rank ends with the
  * reduction of its own shard].  h_plan: the host blob; d_plan: its device
  * copy (first info.blob_bytes bytes, 16-byte aligned), both unchanged

@@ -25,7 +25,7 @@ EXPORTS = ("tide_abi_version", "tide_status_str", "tide_desc_size", "tide_desc_g
            "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams",
            "tide_rs_bf16_to_fp32_census", "tide_ag_place_dma", "tide_dma_engine_count",
            "tide_rs_stage_dma", "tide_rs_fold_staged", "tide_rs_tiles_to_stage",
-           "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma")
+           "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles")
 
 
 class TideShape(ctypes.Structure):
@@ -90,6 +90,7 @@ def lib():
                                   ctypes.POINTER(vp), vp, ctypes.c_size_t,
                                   ctypes.POINTER(TidePlanInfo)]
     L.tide_plan_query.argtypes = [vp, ctypes.POINTER(TidePlanInfo)]
+    L.tide_plan_rank_tiles.argtypes = [vp, i32, i64p, i64p]
     L.tide_rs_bf16_to_fp32.argtypes = [vp, vp, i32, i32, vp]
     L.tide_rs_bf16_to_fp32_tiles.argtypes = [vp, vp, i32, i64, i64, i32, vp]
     L.tide_ag_place.argtypes = [vp, vp, i32, vp]
@@ -111,7 +112,7 @@ def lib():
                  "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams",
                  "tide_rs_bf16_to_fp32_census", "tide_ag_place_dma", "tide_dma_engine_count",
                  "tide_rs_stage_dma", "tide_rs_fold_staged", "tide_rs_tiles_to_stage",
-                 "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma"):
+                 "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles"):
         getattr(L, name).restype = ctypes.c_int
     if L.tide_abi_version() != 1:
         raise RuntimeError("libtide ABI version %d, expected 1" % L.tide_abi_version())

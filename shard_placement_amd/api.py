@@ -104,6 +104,14 @@ def tide_desc_build(shapes, R: int, grad_ptrs=None, out_ptrs=None, gathered_ptr=
     return blob, info
 
 
+def tide_plan_rank_tiles(h_plan: np.ndarray, r: int) -> Tuple[int, int]:
+    """(tile_begin, tile_count) of output rank r's reduce-scatter tiles."""
+    b, c = ctypes.c_int64(0), ctypes.c_int64(0)
+    check(_lib.lib().tide_plan_rank_tiles(h_plan.ctypes.data, int(r), ctypes.byref(b), ctypes.byref(c)),
+          "tide_plan_rank_tiles")
+    return int(b.value), int(c.value)
+
+
 def tide_rs_bf16_to_fp32(h_plan: np.ndarray, d_plan: torch.Tensor, order: int = 0,
                          max_workgroups: int = 0, stream=None) -> None:
     check(_lib.lib().tide_rs_bf16_to_fp32(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
@@ -316,6 +324,13 @@ class Plan:
                                        min(chunk_tiles, n - b), max_workgroups, stream)
             launches += 1
         return launches
+
+    def rs_rank(self, r: int, order: str = "fixed", max_workgroups: int = 0, stream=None) -> None:
+        """Only output rank r's shards (one contiguous tile range)."""
+        b, c = tide_plan_rank_tiles(self.blob, r)
+        if c:
+            tide_rs_bf16_to_fp32_tiles(self.blob, self.d_blob, ORDERS[order], b, c, max_workgroups,
+                                       stream)
 
     def rs_census(self, order: str = "fixed", max_workgroups: int = 0, stream=None) -> torch.Tensor:
         """The reduce-scatter, returning for every tile the packed id of the

@@ -10,6 +10,7 @@
 // in tide.h (rows split in R chunks of ceil(d0/R), +0.0 padding rows,
 // arena offsets rounded up to align_elems).
 #include <algorithm>
+#include <cstddef>
 #include <cstring>
 #include <vector>
 
@@ -530,6 +531,31 @@ tide_status tide_plan_query(const void* h_plan, tide_plan_info* info) {
     info->blob_bytes = (int64_t)h.bytes;
     info->rs_launch_tiles = h.rs_launch_tiles;
     info->ag_launch_tiles = h.ag_launch_tiles;
+    return TIDE_OK;
+}
+
+tide_status tide_plan_rank_tiles(const void* h_plan, int32_t r, int64_t* tile_begin,
+                                 int64_t* tile_count) {
+    if (!h_plan || !tile_begin || !tile_count) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (!h.has_rs) return TIDE_EUNSUPPORTED;
+    if (r < 0 || r >= h.R) return TIDE_EINVAL;
+    // tiles are ordered rank-outer: the first tile of a rank >= x by bisection
+    const RsTile* t = reinterpret_cast<const RsTile*>(static_cast<const uint8_t*>(h_plan) + h.off_rs);
+    auto first_at_least = [&](int32_t x) {
+        int64_t lo = 0, hi = h.n_rs_tiles;
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            int32_t mr;
+            std::memcpy(&mr, reinterpret_cast<const uint8_t*>(t + mid) + offsetof(RsTile, r), sizeof mr);
+            if (mr < x) lo = mid + 1; else hi = mid;
+        }
+        return lo;
+    };
+    *tile_begin = first_at_least(r);
+    *tile_count = first_at_least(r + 1) - *tile_begin;
     return TIDE_OK;
 }
 

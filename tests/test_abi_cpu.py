@@ -407,3 +407,28 @@ def test_pipeline_phases_validate_before_touching_the_gpu():
     assert dcall(plan=np.zeros(4096, np.uint8)) == -7 and dcall(cnt=0, elems=0) == 0
     assert L.tide_rs_tiles_to_stage(blob.ctypes.data, None, 0, n, ctypes.c_void_p(stage), n * T, 0,
                                     None) == -1                   # no device plan
+
+
+@pytest.mark.parametrize("R", [1, 3, 8, 17, 64])
+def test_rank_tile_ranges_partition_the_plan(R):
+    """Rank r's tiles are one contiguous range, the ranges follow each other
+    in rank order and cover every tile; validation on the host."""
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S)
+    blob, info = api.tide_desc_build(SHAPES, R, g, o, ga, f, rs_tile=2048)
+    _, _, _, rs, _ = decode(blob)
+    pos = 0
+    for r in range(R):
+        b, c = api.tide_plan_rank_tiles(blob, r)
+        assert b == pos
+        assert all(int(t["r"]) == r for t in rs[b:b + c])
+        pos = b + c
+    assert pos == int(info.rs_tiles)
+    L = _lib.lib()
+    b, c = ctypes.c_int64(), ctypes.c_int64()
+    assert L.tide_plan_rank_tiles(blob.ctypes.data, R, ctypes.byref(b), ctypes.byref(c)) == -1
+    assert L.tide_plan_rank_tiles(blob.ctypes.data, -1, ctypes.byref(b), ctypes.byref(c)) == -1
+    ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
+    assert L.tide_plan_rank_tiles(ag_blob.ctypes.data, 0, ctypes.byref(b), ctypes.byref(c)) == -6
+    assert L.tide_plan_rank_tiles(np.zeros(4096, np.uint8).ctypes.data, 0, ctypes.byref(b),
+                                  ctypes.byref(c)) == -7

@@ -218,6 +218,26 @@ def test_chunked_launches_same_bits(chunk):
     gu.check_rs_full(st)
 
 
+@pytest.mark.parametrize("R", [1, 3, 8, 64])
+def test_one_call_per_rank_same_bits(R):
+    """Each output rank's shards as one tile-range call (what one GPU of a
+    real job would run), in any order of ranks: the same bits."""
+    w = _wl([(1001, 24), (5,), (64, 64), ()], R, key=180 + R)
+    st = harness.setup(w, with_ag=False)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    gu.say("per-rank calls", R)
+    for r in reversed(range(R)):
+        st.plan.rs_rank(r)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert torch.equal(st.out[r].view(torch.int32), ref[r].view(torch.int32)), r
+    gu.check_rs_full(st)
+
+
 @pytest.mark.parametrize("launch_mib", [-1, 1, 4])
 def test_launch_size_same_bits(launch_mib):
     """A call cut into many launches (or made in one) gives the same bits;
