@@ -328,9 +328,25 @@ def cpu_baseline(st, budget_s: float, max_passes: int = 3):
             oracle.rs([shp], w.R, g)
         passes.append(time.perf_counter() - t0)
     best = min(passes)
+    cores = oracle.max_threads()
+    # one thread on the same sample, when that fits the budget (else on the
+    # first param of it)
+    one_sample = kept if best * cores <= budget_s else kept[:1]
+    one_bytes = sum(w.R * int(np.prod(shp)) * 2 + int(np.prod(shp)) * 4 if len(shp) else w.R * 2 + 4
+                    for shp, _ in one_sample)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        for shp, g in one_sample:
+            oracle.rs([shp], w.R, g)
+        t_one = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
     return {
         "value": round(nbytes / best / 1e9, 3), "unit": "GB/s",
-        "cores": oracle.max_threads(), "kind": "oracle",
+        "cores": cores, "kind": "oracle",
+        "one_thread": {"value": round(one_bytes / t_one / 1e9, 3), "unit": "GB/s",
+                       "sample": "%d of the sample's params, one pass" % len(one_sample)},
         "sample": "reduce-scatter of params %s of %s (R=%d, %.2f GB algorithmic; best of %d "
                   "passes, %.2f s; device->host copy %.1f s not counted); GPU shards of these "
                   "params bit-exact: %s" % (
