@@ -432,3 +432,13 @@ def test_rank_tile_ranges_partition_the_plan(R):
     assert L.tide_plan_rank_tiles(ag_blob.ctypes.data, 0, ctypes.byref(b), ctypes.byref(c)) == -6
     assert L.tide_plan_rank_tiles(np.zeros(4096, np.uint8).ctypes.data, 0, ctypes.byref(b),
                                   ctypes.byref(c)) == -7
+
+
+def test_stream_calls_validate_before_touching_the_gpu():
+    L = _lib.lib()
+    out = ctypes.c_void_p(0)
+    assert L.tide_stream_create_cu_limited(0, ctypes.byref(out)) == -1
+    assert L.tide_stream_create_cu_limited(-3, ctypes.byref(out)) == -1
+    assert L.tide_stream_create_cu_limited(8, None) == -1
+    assert L.tide_stream_destroy(None) == -1
+    assert L.tide_dma_engine_count(None) == -1

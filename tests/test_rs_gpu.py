@@ -311,6 +311,14 @@ def test_cu_census_same_bits_and_counts():
         api.tide_stream_destroy(s)
 
 
+def test_cu_limited_stream_bounds():
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    with pytest.raises(api.TideError):
+        api.tide_stream_create_cu_limited(ncu + 1)
+    s = api.tide_stream_create_cu_limited(ncu)
+    api.tide_stream_destroy(s)
+
+
 def test_deterministic_repeat():
     w = _wl([(4096, 256), (7,)], 16, key=170, sigma=1e-3)
     st = harness.setup(w, with_ag=False)
