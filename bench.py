@@ -204,28 +204,45 @@ def pipeline_leg(st, fused_ms: float) -> dict:
     t1 = ev_time(lambda: api.tide_rs_tiles_to_stage(plan.blob, plan.d_blob, 0, n, full))
     t2 = {"cu": ev_time(lambda: api.tide_rs_stage_to_shards(plan.blob, plan.d_blob, 0, n, full)),
           "sdma": ev_time(lambda: api.tide_rs_stage_to_shards_sdma(plan.blob, 0, n, full), reps=1)}
-    # phase 2 confined to a few CUs: a consumer with a link's bandwidth
-    link_cus = 8
-    s8 = api.tide_stream_create_cu_limited(link_cus)
+    # phase 2 confined to a few CUs: a consumer with a link's bandwidth (8
+    # CUs) or with a quarter of the chip (64); in the pipeline phase 1 then
+    # runs on the other CUs
+    link = {"cu64": 64, "cu8": 8}
+    # phase 1 alone on a stream of the pipeline's kind (CU-masked, all CUs)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sm = api.tide_stream_create_cu_limited(n_cu)
     try:
-        with torch.cuda.stream(s8):
-            t2["cu%d" % link_cus] = ev_time(
-                lambda: api.tide_rs_stage_to_shards(plan.blob, plan.d_blob, 0, n, full, stream=s8),
-                reps=1)
+        with torch.cuda.stream(sm):
+            t1_masked = ev_time(lambda: api.tide_rs_tiles_to_stage(plan.blob, plan.d_blob, 0, n, full,
+                                                                  stream=sm))
     finally:
         torch.cuda.synchronize()
-        api.tide_stream_destroy(s8)
+        api.tide_stream_destroy(sm)
+    for name, k in link.items():
+        sk = api.tide_stream_create_cu_limited(k)
+        try:
+            with torch.cuda.stream(sk):
+                t2[name] = ev_time(
+                    lambda: api.tide_rs_stage_to_shards(plan.blob, plan.d_blob, 0, n, full, stream=sk),
+                    reps=1)
+        finally:
+            torch.cuda.synchronize()
+            api.tide_stream_destroy(sk)
     del full
     torch.cuda.empty_cache()
     runs = []
     same = True
-    for phase2 in ("cu", "sdma", "cu%d" % link_cus):
+    for phase2 in ("cu", "sdma", "cu64", "cu8"):
         for mult, depth in ((0.25, 2), (1, 1), (1, 2), (1, 4), (4, 2)):
             chunk = max(1, int(L * mult))
             tp = pipeline.TwoPhase(plan, chunk, depth, "sdma" if phase2 == "sdma" else "cu",
-                                   link_cus if phase2 != "cu" and phase2 != "sdma" else 0)
+                                   link.get(phase2, 0))
             try:
-                t = ev_time(tp.run, reps=1 if phase2 != "cu" else 2)
+                t = ev_time(tp.run, reps=2 if phase2 == "cu" else 1)
+                h0 = time.perf_counter()
+                tp.run()
+                host_ms = (time.perf_counter() - h0) * 1e3
+                torch.cuda.synchronize()
             finally:
                 tp.close()
             same = same and all(torch.equal(o[: st.S].view(torch.int32), r.view(torch.int32))
@@ -233,16 +250,17 @@ def pipeline_leg(st, fused_ms: float) -> dict:
             serial = t1 + t2[phase2]
             runs.append({"phase2": phase2, "chunk_tiles": chunk, "depth": depth,
                          "staging_mib": round(tp.staging_bytes / 2 ** 20, 1), "ms": round(t, 3),
+                         "host_issue_ms": round(host_ms, 3),
                          "overlap": round((serial - t) / min(t1, t2[phase2]), 3)})
             del tp
     del ref
     torch.cuda.empty_cache()
-    return {"phase1_ms": round(t1, 4), "phase2_cu_ms": round(t2["cu"], 4),
-            "phase2_sdma_ms": round(t2["sdma"], 3),
-            "phase2_cu%d_ms" % link_cus: round(t2["cu%d" % link_cus], 3), "fused_ms": round(fused_ms, 4),
-            "layer_staging_mib": round(n * T * 4 / 2 ** 20, 1), "runs": runs,
-            "same_bits_as_fused": bool(same),
-            "overlap_def": "(phase1 alone + phase2 alone - pipelined) / min(phase1, phase2)"}
+    out = {"phase1_ms": round(t1, 4), "phase1_masked_stream_ms": round(t1_masked, 4)}
+    out.update({"phase2_%s_ms" % k: round(v, 4) for k, v in t2.items()})
+    out.update({"fused_ms": round(fused_ms, 4), "layer_staging_mib": round(n * T * 4 / 2 ** 20, 1),
+                "runs": runs, "same_bits_as_fused": bool(same),
+                "overlap_def": "(phase1 alone + phase2 alone - pipelined) / min(phase1, phase2)"})
+    return out
 
 
 def stock_leg(st, rsb: int, agb: int, reps: int = 3) -> dict:

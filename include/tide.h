@@ -49,7 +49,8 @@
  * tide_rs_stage_dma) are host-synchronous instead (they wait for the
  * caller's stream, then for their copies).  The only state kept between
  * calls is, per device, the ROCr agent and copy-engine list those calls look
- * up once (guarded by a mutex).  A plan holds raw device addresses: it is
+ * up once (guarded by a mutex).  Streams and pipeline objects the library
+ * creates on request are the caller's to release.  A plan holds raw device addresses: it is
  * invalid once any of them is freed.
  *
  * Errors: every entry point returns a tide_status; nothing is thrown
@@ -318,7 +319,46 @@ tide_status tide_rs_stage_to_shards_sdma(const void *h_plan, int64_t tile_begin,
  * n_cu in [1, number of CUs]; *out receives the stream; release it with
  * tide_stream_destroy.  Creating a stream synchronises nothing. */
 tide_status tide_stream_create_cu_limited(int32_t n_cu, tide_stream_t *out);
+/* The same for the mask bits [first_cu, first_cu + n_cu): two streams with
+ * disjoint ranges never share a compute unit.  first_cu >= 0, n_cu >= 1,
+ * first_cu + n_cu <= number of CUs. */
+tide_status tide_stream_create_cu_range(int32_t first_cu, int32_t n_cu, tide_stream_t *out);
 tide_status tide_stream_destroy(tide_stream_t stream);
+
+/* The two-phase reduce-scatter pipeline, with its chunk loop issued by the
+ * library [Abstract: the reduce-scatter runs as a two-phase pipeline whose
+ * staging stays nearly constant; kongchang.com "Performance"].  Chunk i of
+ * chunk_tiles plan tiles is reduced (tide_rs_tiles_to_stage) into slot
+ * i % depth of a caller-owned ring of depth slots of chunk_tiles * rs_tile
+ * floats, then moved to the shard arenas by phase 2 (phase2 = 0: the
+ * tide_rs_stage_to_shards kernel; 1: the copy-kind copies of
+ * tide_rs_stage_to_shards_sdma).  The phases run on two streams of the
+ * pipeline object, each with a hardware queue of its own, ordered per slot
+ * by events: phase 2 of chunk i after its phase 1, phase 1 of chunk i after
+ * phase 2 of chunk i - depth.  The result is bit-identical to
+ * tide_rs_bf16_to_fp32 with order 0.
+ *
+ * tide_pipeline_create: depth in [1, 64]; phase2_cus = 0 lets both phases
+ * use every CU, phase2_cus = k in [1, CUs) confines phase 2 to the mask
+ * bits [0, k) (a consumer with a link's bandwidth) and phase 1 to the rest.
+ * Creates two streams and 2 * depth + 3 events on the current device;
+ * allocates no device memory.  tide_pipeline_destroy waits for the two
+ * streams and releases them (the device is made current for the call).
+ *
+ * tide_pipeline_run: on the object's device; ring 16-byte aligned, at least
+ * min(depth, chunks) * chunk_tiles * rs_tile floats (chunk_tiles is clamped
+ * to the plan's tile count), overlapping no gradient or arena; phase2 = 1
+ * only with phase2_cus = 0.  Ordered after the earlier work of `stream` and
+ * before its later work; asynchronous.  All checks are made before anything
+ * is issued.  Calls on one object must not overlap in time from several
+ * host threads; calls issued one after another on the same stream may
+ * share the ring. */
+typedef struct tide_pipeline *tide_pipeline_t;
+tide_status tide_pipeline_create(int32_t depth, int32_t phase2_cus, tide_pipeline_t *out);
+tide_status tide_pipeline_run(tide_pipeline_t pipeline, const void *h_plan, const void *d_plan,
+                              int64_t chunk_tiles, float *ring, int64_t ring_elems,
+                              int32_t phase2, tide_stream_t stream);
+tide_status tide_pipeline_destroy(tide_pipeline_t pipeline);
 
 /* Static text for a status code. */
 const char *tide_status_str(int32_t status);

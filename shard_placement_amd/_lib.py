@@ -25,7 +25,9 @@ EXPORTS = ("tide_abi_version", "tide_status_str", "tide_desc_size", "tide_desc_g
            "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams",
            "tide_rs_bf16_to_fp32_census", "tide_ag_place_dma", "tide_dma_engine_count",
            "tide_rs_stage_dma", "tide_rs_fold_staged", "tide_rs_tiles_to_stage",
-           "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles")
+           "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles",
+           "tide_stream_create_cu_range", "tide_pipeline_create", "tide_pipeline_run",
+           "tide_pipeline_destroy")
 
 
 class TideShape(ctypes.Structure):
@@ -106,13 +108,19 @@ def lib():
     L.tide_rs_tiles_to_stage.argtypes = [vp, vp, i64, i64, vp, i64, i32, vp]
     L.tide_rs_stage_to_shards.argtypes = [vp, vp, i64, i64, vp, i64, i32, vp]
     L.tide_rs_stage_to_shards_sdma.argtypes = [vp, i64, i64, vp, i64, vp]
+    L.tide_stream_create_cu_range.argtypes = [i32, i32, ctypes.POINTER(vp)]
+    L.tide_pipeline_create.argtypes = [i32, i32, ctypes.POINTER(vp)]
+    L.tide_pipeline_run.argtypes = [vp, vp, vp, i64, vp, i64, i32, vp]
+    L.tide_pipeline_destroy.argtypes = [vp]
     for name in ("tide_desc_size", "tide_desc_geometry", "tide_desc_build", "tide_plan_query",
                  "tide_rs_bf16_to_fp32", "tide_ag_place", "tide_ag_place_sdma",
                  "tide_stream_create_cu_limited", "tide_stream_destroy",
                  "tide_rs_bf16_to_fp32_tiles", "tide_ag_place_sdma_streams",
                  "tide_rs_bf16_to_fp32_census", "tide_ag_place_dma", "tide_dma_engine_count",
                  "tide_rs_stage_dma", "tide_rs_fold_staged", "tide_rs_tiles_to_stage",
-                 "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles"):
+                 "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles",
+                 "tide_stream_create_cu_range", "tide_pipeline_create", "tide_pipeline_run",
+                 "tide_pipeline_destroy"):
         getattr(L, name).restype = ctypes.c_int
     if L.tide_abi_version() != 1:
         raise RuntimeError("libtide ABI version %d, expected 1" % L.tide_abi_version())

@@ -227,6 +227,39 @@ def tide_stream_create_cu_limited(n_cu: int) -> torch.cuda.ExternalStream:
     return torch.cuda.ExternalStream(int(h.value))
 
 
+def tide_stream_create_cu_range(first_cu: int, n_cu: int) -> torch.cuda.ExternalStream:
+    """A torch stream wrapping a HIP stream confined to CU mask bits
+    [first_cu, first_cu + n_cu).  Release it with tide_stream_destroy."""
+    h = ctypes.c_void_p(0)
+    check(_lib.lib().tide_stream_create_cu_range(int(first_cu), int(n_cu), ctypes.byref(h)),
+          "tide_stream_create_cu_range")
+    return torch.cuda.ExternalStream(int(h.value))
+
+
+def tide_pipeline_create(depth: int, phase2_cus: int = 0) -> int:
+    """Handle of a two-phase pipeline object (two streams, per-slot events)
+    on the current device; release it with tide_pipeline_destroy."""
+    h = ctypes.c_void_p(0)
+    check(_lib.lib().tide_pipeline_create(int(depth), int(phase2_cus), ctypes.byref(h)),
+          "tide_pipeline_create")
+    return int(h.value)
+
+
+def tide_pipeline_run(handle: int, h_plan: np.ndarray, d_plan: torch.Tensor, chunk_tiles: int,
+                      ring: torch.Tensor, phase2: int = 0, stream=None) -> None:
+    """The whole reduce-scatter through the pipeline, ordered on ``stream``
+    (default: the current stream)."""
+    _require(ring, torch.float32, "ring")
+    check(_lib.lib().tide_pipeline_run(ctypes.c_void_p(handle), h_plan.ctypes.data,
+                                       d_plan.data_ptr(), int(chunk_tiles), ring.data_ptr(),
+                                       ring.numel(), int(phase2), _stream(stream)),
+          "tide_pipeline_run")
+
+
+def tide_pipeline_destroy(handle: int) -> None:
+    check(_lib.lib().tide_pipeline_destroy(ctypes.c_void_p(handle)), "tide_pipeline_destroy")
+
+
 def tide_stream_destroy(stream) -> None:
     check(_lib.lib().tide_stream_destroy(ctypes.c_void_p(int(stream.cuda_stream))),
           "tide_stream_destroy")

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtide.so")
-SOURCES = ["plan.cpp", "rs.hip", "ag.hip", "dma.cpp"]
+SOURCES = ["plan.cpp", "rs.hip", "ag.hip", "dma.cpp", "pipeline.cpp"]
 LIBS = ["-L/opt/rocm/lib", "-lhsa-runtime64"]  # ROCr, for the copy engines
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -285,29 +285,6 @@ extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_onl
     return TIDE_OK;
 }
 
-extern "C" tide_status tide_stream_create_cu_limited(int32_t n_cu, tide_stream_t* out) {
-    if (!out || n_cu < 1) return TIDE_EINVAL;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return TIDE_EHIP;
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TIDE_EHIP;
-    const int ncu = prop.multiProcessorCount;
-    if (n_cu > ncu) return TIDE_EINVAL;
-    uint32_t mask[64] = {0};
-    const int words = (ncu + 31) / 32;
-    if (words > 64) return TIDE_EUNSUPPORTED;
-    for (int i = 0; i < n_cu; ++i) mask[i / 32] |= 1u << (i % 32);
-    hipStream_t s = nullptr;
-    if (hipExtStreamCreateWithCUMask(&s, (uint32_t)words, mask) != hipSuccess) return TIDE_EHIP;
-    *out = reinterpret_cast<tide_stream_t>(s);
-    return TIDE_OK;
-}
-
-extern "C" tide_status tide_stream_destroy(tide_stream_t stream) {
-    if (!stream) return TIDE_EINVAL;
-    return hipStreamDestroy(reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? TIDE_OK : TIDE_EHIP;
-}
-
 extern "C" tide_status tide_ag_place_sdma_streams(const void* h_plan, const tide_stream_t* streams,
                                                   int32_t n_streams) {
     if (!h_plan || !streams || n_streams < 1 || n_streams > 64) return TIDE_EINVAL;

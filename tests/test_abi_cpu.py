@@ -440,5 +440,16 @@ def test_stream_calls_validate_before_touching_the_gpu():
     assert L.tide_stream_create_cu_limited(0, ctypes.byref(out)) == -1
     assert L.tide_stream_create_cu_limited(-3, ctypes.byref(out)) == -1
     assert L.tide_stream_create_cu_limited(8, None) == -1
+    assert L.tide_stream_create_cu_range(-1, 8, ctypes.byref(out)) == -1
+    assert L.tide_stream_create_cu_range(0, 0, ctypes.byref(out)) == -1
+    assert L.tide_stream_create_cu_range(0, 8, None) == -1
     assert L.tide_stream_destroy(None) == -1
     assert L.tide_dma_engine_count(None) == -1
+    # the pipeline object: argument checks come before any device query
+    assert L.tide_pipeline_create(0, 0, ctypes.byref(out)) == -1
+    assert L.tide_pipeline_create(65, 0, ctypes.byref(out)) == -1
+    assert L.tide_pipeline_create(2, -1, ctypes.byref(out)) == -1
+    assert L.tide_pipeline_create(2, 0, None) == -1
+    fake = ctypes.c_void_p(1 << 44)
+    assert L.tide_pipeline_run(None, None, fake, 4, fake, 1 << 20, 0, None) == -1
+    assert L.tide_pipeline_destroy(None) == -1

@@ -98,3 +98,75 @@ def test_full_size_pipeline_matches_in_place(phase2):
     del ref, tp
     st.free()
     torch.cuda.empty_cache()
+
+
+def test_object_reused_across_calls_and_streams():
+    """One pipeline object, two runs with a clearing of the arenas between
+    them on the caller's stream, then a run on a side stream: the caller's
+    work is ordered around each run (no host synchronisation in between)."""
+    shapes = [(1001, 24), (4096, 96), (96,), (5,), ()]
+    R = 5
+    w = _wl(shapes, R, 960, sigma=1e-3)
+    st = harness.setup(w, with_ag=False)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    tp = pipeline.TwoPhase(st.plan, 3, 2, "cu", 0)
+    try:
+        gu.say("pipeline reuse", tp.chunks())
+        for o in st.out:
+            o.view(torch.int32).fill_(-1)
+        tp.run()
+        for o in st.out:
+            o.view(torch.int32).fill_(-1)
+        tp.run()
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert torch.equal(st.out[r].view(torch.int32), ref[r].view(torch.int32)), r
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            for o in st.out:
+                o.view(torch.int32).fill_(-1)
+            tp.run()
+            for r in range(R):
+                st.out[r].view(torch.int32).sub_(ref[r].view(torch.int32))
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert int(st.out[r].view(torch.int32).abs().max()) == 0, r
+    finally:
+        tp.close()
+    gu.check_out_guards(st, 0)
+
+
+def test_run_validates_before_issuing():
+    shapes = [(4096, 96), (96,)]
+    R = 4
+    w = _wl(shapes, R, 961)
+    st = harness.setup(w, with_ag=False)
+    n, T = int(st.plan.info.rs_tiles), int(st.plan.info.rs_tile_elems)
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    h = api.tide_pipeline_create(2, 0)
+    h8 = api.tide_pipeline_create(2, 8)
+    try:
+        assert st.S >= 2 * T and n > 6
+        ring = torch.empty(2 * 2 * T, dtype=torch.float32, device="cuda")
+        with pytest.raises(api.TideError) as e:         # ring smaller than two slots of 3 tiles
+            api.tide_pipeline_run(h, st.plan.blob, st.plan.d_blob, 3, ring)
+        assert e.value.status == -1
+        with pytest.raises(api.TideError) as e:         # the ring over rank 1's arena
+            api.tide_pipeline_run(h, st.plan.blob, st.plan.d_blob, 1, st.out[1][: 2 * T])
+        assert e.value.status == -3
+        with pytest.raises(api.TideError) as e:         # copies on a CU-confined pipeline
+            api.tide_pipeline_run(h8, st.plan.blob, st.plan.d_blob, 1, ring, phase2=1)
+        assert e.value.status == -1
+        with pytest.raises(api.TideError) as e:         # not 16-byte aligned
+            api.tide_pipeline_run(h, st.plan.blob, st.plan.d_blob, 1, ring[1:])
+        assert e.value.status == -2
+        torch.cuda.synchronize()
+        # nothing was issued: the arenas still hold the fill
+        assert all(bool(o.view(torch.int32).eq(-1).all()) for o in st.out)
+        gu.say("pipeline validation", n)
+    finally:
+        api.tide_pipeline_destroy(h)
+        api.tide_pipeline_destroy(h8)
