@@ -85,13 +85,17 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
             t0m = _median([e0.elapsed_time(e1) for e0, e1 in own])
             # concurrent: enough reduce-scatters to cover the GEMM train twice
             n_rs = max(2, int(2.0 * iters * t0m / rs_alone) + 2)
+            # the GEMM train is queued right after the first reduce-scatter
+            # call, so that its queue holds work while the reduce-scatter
+            # runs however long the host takes to issue the rest
             r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             r0.record(rs_stream)
-            for _ in range(n_rs):
-                plan.rs(max_workgroups=max_wg, stream=rs_stream)
-            r1.record(rs_stream)
+            plan.rs(max_workgroups=max_wg, stream=rs_stream)
             gemm_stream.wait_event(r0)
             conc = _gemm_train(a, b, c, gemm_stream, iters)
+            for _ in range(n_rs - 1):
+                plan.rs(max_workgroups=max_wg, stream=rs_stream)
+            r1.record(rs_stream)
             torch.cuda.synchronize()
             window = r0.elapsed_time(r1)
             inside = [e1.elapsed_time(e2) for e1, e2 in conc
