@@ -88,9 +88,6 @@ __device__ __forceinline__ void acc_add(float (&a)[8], u32x4 v) {
     a[6] = a[6] + bf_lo(v.w); a[7] = a[7] + bf_hi(v.w);
 }
 
-
-
-
 // The compute unit a workgroup runs on, for the optional census: the HW_ID
 // hardware register's cu_id [11:8], sh_id [12] and se_id [15:13] fields
 // and the XCC_ID register's xcc_id [3:0], packed as xcc << 8 | (HW_ID >> 8
