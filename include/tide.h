@@ -220,8 +220,10 @@ tide_status tide_ag_place(const void *h_plan, const void *d_plan,
 /* The same placement issued as host-side copies from the host plan,
  * asynchronous on `stream` [Abstract: no SMs used for placement].
  * engine_only = 1: one 1-D copy per (param, rank) run with the runtime's
- * no-compute-unit copy kind (hipMemcpyDeviceToDeviceNoCU): the DMA engines
- * move the data, no kernel runs.  engine_only = 0: at most two copies per
+ * no-compute-unit copy kind (hipMemcpyDeviceToDeviceNoCU); the runtime
+ * picks the engine: usually the DMA engines, but it has also been seen to
+ * run such copies as small blit kernels, so only tide_ag_place_dma is
+ * guaranteed to use no compute unit.  engine_only = 0: at most two copies per
  * param (a 2-D copy over the ranks with full shards, a 1-D copy for the
  * partial rank) of the ordinary device-to-device kind, which the runtime
  * executes with a blit kernel. */
@@ -231,7 +233,8 @@ tide_status tide_ag_place_sdma(const void *h_plan, int32_t engine_only,
 /* The engine-only placement with its copies spread over n_streams streams
  * (largest first, each to the stream with the fewest bytes so far), so
  * that several DMA engines can work at once.  The caller orders the
- * streams against its other work (e.g. with events); no kernel runs. */
+ * streams against its other work (e.g. with events).  Same copy kind, and
+ * the same caveat, as engine_only = 1 above. */
 tide_status tide_ag_place_sdma_streams(const void *h_plan, const tide_stream_t *streams,
                                        int32_t n_streams);
 

@@ -258,9 +258,10 @@ extern "C" tide_status tide_ag_place_sdma(const void* h_plan, int32_t engine_onl
         const int64_t nfull = d.d0 / d.s;        // ranks whose shard has s valid rows
         const int64_t rest = d.n - nfull * d.m;  // elements of the one partial rank
         if (engine_only) {
-            // One 1-D copy per (param, rank) run: the runtime's no-compute-
-            // unit copy kind puts these on the DMA engines (a 2-D copy of
-            // the same kind is executed by a blit kernel).
+            // One 1-D copy per (param, rank) run of the runtime's no-compute-
+            // unit copy kind, which the runtime normally gives to the DMA
+            // engines (a 2-D copy of the same kind is always executed by a
+            // blit kernel, and 1-D ones have been seen to be too).
             const int64_t nruns = nfull + (rest > 0 ? 1 : 0);
             for (int64_t r = 0; r < nruns && r < h.R; ++r) {
                 const int64_t cnt = r < nfull ? d.m : rest;
