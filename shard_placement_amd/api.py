@@ -15,7 +15,7 @@ writes a rank-major bf16 gathered buffer into per-parameter tensors.
 from __future__ import annotations
 
 import ctypes
-from typing import List, Optional, Sequence, Tuple
+from typing import Sequence, Tuple
 
 import numpy as np
 import torch

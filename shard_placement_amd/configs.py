@@ -9,7 +9,7 @@ first dimension is the one that is sharded.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Tuple
 
 Shape = Tuple[int, ...]

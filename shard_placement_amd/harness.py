@@ -7,7 +7,7 @@ data-path work is done by the library through ``api``.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Optional
 
 import torch

@@ -10,7 +10,6 @@ import numpy as np
 import torch
 
 import oracle
-from shard_placement_amd import synth
 
 NAN32 = 0xFFFFFFFF
 SENT16 = 0xFFFF

@@ -6,7 +6,6 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from shard_placement_amd import api, configs, harness
 from tests import gpu_util as gu
 
