@@ -614,10 +614,14 @@ def main():
         "rs_gbps": round(rs_gbs, 1),
         "rs_frac_hbm": round(rs_gbs / HBM_PEAK_GBS, 4),
         "rs_ms": round(rs_avg, 4),
+        "rs_ms_median": round(sorted(rs_ms)[len(rs_ms) // 2], 4),
+        "rs_ms_min": round(min(rs_ms), 4),
         "rs_tree_gbps": round(rsb / (tree_ms * 1e-3) / 1e9, 1),
         "ag_gbps": round(ag_gbs, 1),
         "ag_frac_hbm": round(ag_gbs / HBM_PEAK_GBS, 4),
         "ag_ms": round(ag_avg, 4),
+        "ag_ms_median": round(sorted(ag_ms)[len(ag_ms) // 2], 4),
+        "ag_ms_min": round(min(ag_ms), 4),
         "ag_sdma": sdma,
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
