@@ -151,6 +151,28 @@ def check_rs_sampled(st, order="fixed", per_shard=64, edge=16, seed=0):
     return checked
 
 
+def check_rs_points(st, p, flat, order="fixed"):
+    """Bit-exact oracle comparison at given flat element indices of param p
+    (each in the shard of rank j // m at element j % m); returns the count."""
+    w = st.w
+    R = w.R
+    _, m, off, _ = oracle.layout(w.shapes, R, _align_of(st))
+    mp, n = int(m[p]), numel(w.shapes[p])
+    j = np.unique(np.asarray(flat, np.int64))
+    assert mp > 0 and j.size and j.min() >= 0 and j.max() < n
+    dev = st.out[0].device
+    rr, ii = j // mp, j % mp
+    got = np.empty(j.size, np.uint32)
+    for r in np.unique(rr):
+        sel = np.flatnonzero(rr == r)
+        got[sel] = bits32(st.out[int(r)][torch.from_numpy(int(off[p]) + ii[sel]).to(dev)])
+    jv = torch.from_numpy(j).to(dev)
+    vals = torch.stack([st.grads[q][p].reshape(-1)[jv] for q in range(R)], dim=1)
+    want = oracle.fold_points(bits16(vals).reshape(-1, R), order).view(np.uint32)
+    assert_bits_equal(got, want, "%s param %d points" % (w.name, p))
+    return j.size
+
+
 def check_rs_bound_all(st, order="fixed"):
     """Every element of every shard, at any size: within the summation error
     bound of the exact sum (gamma_{R-1} for rank order, gamma_{ceil log2 R}

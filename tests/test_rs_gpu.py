@@ -430,3 +430,37 @@ def test_full_size_workload(key):
     st.free()
     del snap
     torch.cuda.empty_cache()
+
+
+@pytest.mark.big
+def test_offsets_beyond_2_pow_31():
+    """A ragged 2-D param of 2^31 + 98,304 elements (byte offsets past 4 GiB
+    in the gradients, past 2^31 elements in the gathered buffer) at R = 3:
+    rank 2 keeps 21,845 valid rows and 2 padding rows.  Elements straddling
+    flat index 2^31 and every shard's edges against the oracle, every
+    element within the summation bound, the placement in full."""
+    w = _wl([(65539, 32768), (96,)], 3, key=990, sigma=1e-3, name="beyond-2^31")
+    need = _need_gb(w, False)
+    if _free_gb() < need:
+        pytest.skip("needs %.0f GB of free HBM" % need)
+    gu.say("offsets beyond 2^31: need GB", round(need))
+    st = harness.setup(w, guard=64)
+    torch.cuda.synchronize()
+    st.plan.ag()
+    st.plan.rs()
+    torch.cuda.synchronize()
+    n0 = 65539 * 32768
+    pts = np.concatenate([np.arange(2 ** 31 - 64, 2 ** 31 + 64), np.arange(n0 - 64, n0),
+                          np.arange(2 ** 30 - 8, 2 ** 30 + 8)])
+    assert gu.check_rs_points(st, 0, pts) == pts.size
+    gu.check_rs_sampled(st)
+    gu.check_rs_bound_all(st)
+    for r in range(w.R):
+        gu.check_out_guards(st, r)
+    gu.say("offsets beyond 2^31: placement")
+    gu.check_ag_full(st)
+    st.plan.rs(order="tree")
+    torch.cuda.synchronize()
+    gu.check_rs_points(st, 0, pts, order="tree")
+    st.free()
+    torch.cuda.empty_cache()
