@@ -211,6 +211,8 @@ def test_validation_errors():
     g, o, ga, f = _fake_ptrs(SHAPES, R, S)
     b = api.tide_desc_build
     assert _status(b, SHAPES, 0, g, o, None, None) == -1          # R < 1
+    assert _status(api.tide_desc_geometry, SHAPES, 4097) == -1    # R above the limit
+    assert _status(api.tide_desc_geometry, SHAPES, 4096) == 0     # the limit itself
     assert _status(b, SHAPES, R, g, None, None, None) == -1       # grads without outputs
     assert _status(b, SHAPES, R, g, o, ga, None) == -1            # gathered without full
     g2 = list(g); g2[0] = 0

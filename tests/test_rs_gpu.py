@@ -98,6 +98,18 @@ def test_tree_order_odd_rank_counts(R):
     gu.check_rs_full(st, "tree")
 
 
+@pytest.mark.parametrize("order", ["fixed", "tree"])
+def test_largest_rank_count(order):
+    """R = 4096, the library's limit (the tree's deepest stack): ragged and
+    all-padding shards, whole arenas against the oracle."""
+    R = 4096
+    w = _wl([(R + 1, 2), (2 * R - 1,), ()], R, key=140)
+    gu.say("R", R, order)
+    st = harness.setup(w, with_ag=False)
+    _run(st, order)
+    gu.check_rs_full(st, order)
+
+
 def _random_problem(seed):
     rng = np.random.default_rng(1000 + seed)
     R = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 23, 32, 64, 70]))
