@@ -132,6 +132,19 @@ def test_fuzz_random_placements(seed):
         assert np.all(f[:16] == gu.SENT16) and np.all(f[16 + n:] == gu.SENT16)
 
 
+@pytest.mark.parametrize("engine", ["cu", "dma"])
+def test_largest_rank_count(engine):
+    """R = 4096, the library's limit: a gathered buffer of 4096 slots, ragged
+    and empty ranks, placed in full and compared with the oracle."""
+    R = 4096
+    w = _wl([(R + 1, 2), (2 * R - 1,), ()], R, key=340)
+    gu.say("ag R", R, engine)
+    st = harness.setup(w, with_rs=False)
+    _place(st.plan, engine)
+    torch.cuda.synchronize()
+    gu.check_ag_full(st)
+
+
 def test_placement_of_rs_output_is_full_fold():
     """AG(bf16(RS shards)) equals bf16 of the full fold, all on the device."""
     shapes = [(1001, 24), (5,), (64, 64)]
