@@ -455,3 +455,19 @@ def test_stream_calls_validate_before_touching_the_gpu():
     fake = ctypes.c_void_p(1 << 44)
     assert L.tide_pipeline_run(None, None, fake, 4, fake, 1 << 20, 0, None) == -1
     assert L.tide_pipeline_destroy(None) == -1
+
+
+def test_empty_layer_issues_nothing():
+    """A layer with no params: the plan has no tiles, and both calls return
+    OK without touching the device (so they run here, with no GPU)."""
+    R = 4
+    outs = [(5 + r) << 40 for r in range(R)]
+    blob, info = api.tide_desc_build([], R, [], outs, None, None)
+    assert int(info.rs_tiles) == 0 and int(info.ag_tiles) == 0
+    L = _lib.lib()
+    fake = ctypes.c_void_p(1 << 44)
+    assert L.tide_rs_bf16_to_fp32(blob.ctypes.data, fake, 0, 0, None) == 0
+    assert L.tide_rs_bf16_to_fp32(blob.ctypes.data, fake, 1, 0, None) == 0
+    b, c = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    assert L.tide_plan_rank_tiles(blob.ctypes.data, R - 1, ctypes.byref(b), ctypes.byref(c)) == 0
+    assert c.value == 0
