@@ -647,6 +647,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, "
                                      "copy-calibrated)"},
         "cpu_baseline": cpu,
+        "env": {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
+                "hip": torch.version.hip, "host_threads": len(os.sched_getaffinity(0))},
     }
     print(json.dumps(rec), flush=True)
     if cpu and cpu.get("parity_mismatches"):
