@@ -471,3 +471,22 @@ def test_empty_layer_issues_nothing():
     b, c = ctypes.c_int64(-1), ctypes.c_int64(-1)
     assert L.tide_plan_rank_tiles(blob.ctypes.data, R - 1, ctypes.byref(b), ctypes.byref(c)) == 0
     assert c.value == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With the library absent the binding raises: there is no fallback path
+    (checked in a fresh interpreter so the loaded library stays untouched)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import shard_placement_amd._lib as L\n"
+            "L.LIB_PATH = %r\n"
+            "from shard_placement_amd import api\n"
+            "try:\n"
+            "    api.tide_desc_geometry([(4, 4)], 2)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "    sys.exit(0)\n"
+            "sys.exit(1)\n") % (ROOT, str(tmp_path / "libtide.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "not built" in r.stdout, r.stdout + r.stderr
