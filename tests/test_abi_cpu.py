@@ -490,3 +490,32 @@ def test_missing_library_fails_loudly(tmp_path):
             "sys.exit(1)\n") % (ROOT, str(tmp_path / "libtide.so"))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "not built" in r.stdout, r.stdout + r.stderr
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package and its native sources neither import, include nor load
+    the oracle; bench.py imports it only inside its cpu_baseline leg."""
+    import ast
+    pkg = os.path.join(ROOT, "shard_placement_amd")
+    for name in os.listdir(pkg):
+        path = os.path.join(pkg, name)
+        if name.endswith(".py"):
+            tree = ast.parse(open(path).read())
+            for node in ast.walk(tree):
+                if isinstance(node, ast.Import):
+                    assert all(a.name.split(".")[0] != "oracle" for a in node.names), name
+                if isinstance(node, ast.ImportFrom):
+                    assert (node.module or "").split(".")[0] != "oracle", name
+    for name in os.listdir(os.path.join(pkg, "csrc")):
+        text = open(os.path.join(pkg, "csrc", name)).read()
+        assert "tide_oracle" not in text and "oracle/" not in text, name
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    users = set()
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef):
+            for node in ast.walk(fn):
+                if isinstance(node, ast.Import) and any(a.name == "oracle" for a in node.names):
+                    users.add(fn.name)
+    top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
+    assert all(not (isinstance(n, ast.Import) and any(a.name == "oracle" for a in n.names)) for n in top)
+    assert users == {"cpu_baseline"}, users
