@@ -519,3 +519,11 @@ def test_product_path_never_touches_the_oracle():
     top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
     assert all(not (isinstance(n, ast.Import) and any(a.name == "oracle" for a in n.names)) for n in top)
     assert users == {"cpu_baseline"}, users
+    # and the other way round: the oracle uses none of the library's code
+    src = open(os.path.join(ROOT, "oracle", "tide_oracle.c")).read()
+    assert "tide.h" not in src and "plan_format" not in src
+    tree = ast.parse(open(os.path.join(ROOT, "oracle", "__init__.py")).read())
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.Import, ast.ImportFrom)):
+            mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+            assert all(not m.startswith("shard_placement_amd") for m in mods)
