@@ -626,6 +626,7 @@ def main():
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "gemm_slowdown_pct": probe["modes"][0]["gemm_slowdown_pct"] if probe else None,
         "rs_launches": n_launch,
+        "rs_lds_per_workgroup": int(info.rs_lds_bytes),
         "rs_cus": cus_measured,
         "rs_cus_per_xcc": {str(k): v for k, v in sorted(per_xcc.items())},
         "rs_cu_ms": round(cus_measured * rs_avg, 1),

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define TIDE_ABI_VERSION 1
+#define TIDE_ABI_VERSION 2
 
 /* A hipStream_t (struct ihipStream_t*); NULL is the null stream. */
 struct ihipStream_t;
@@ -100,9 +100,11 @@ typedef struct tide_opts {
     int32_t launch_mib;    /* algorithmic MiB moved per kernel launch: a call is cut
                               into launches of about this size, so that concurrent
                               kernels on other streams get whole compute units at
-                              the launch boundaries (0: defaults, 160 MiB and at
-                              least 1024 tiles for the reduce-scatter, 256 MiB for
-                              the placement; -1: one launch) */
+                              the launch boundaries (0: defaults, 160 MiB for the
+                              reduce-scatter, rounded down to a multiple of 256
+                              tiles (one per CU) when it holds fewer than 1024,
+                              and at least 512 tiles; 256 MiB for the placement;
+                              -1: one launch; an explicit size is not rounded) */
 } tide_opts;
 
 /* Access hints (results are identical with any combination). */
@@ -121,6 +123,12 @@ typedef struct tide_plan_info {
     int64_t blob_bytes;     /* bytes of the blob in use: upload this many */
     int64_t rs_launch_tiles; /* tiles per reduce-scatter launch */
     int64_t ag_launch_tiles; /* tiles per placement launch */
+    int64_t rs_lds_bytes;    /* LDS each reduce-scatter workgroup holds: 8 KB (what
+                                the kernels use), or 64 KB when a default launch
+                                holds at most 512 tiles (2 workgroups per CU), so
+                                that two fill 128 of the CU's 160 KB and a concurrent
+                                kernel's workgroup needing more than 32 KB cannot
+                                start beside them */
 } tide_plan_info;
 
 /* Size of the plan blob for these shapes (an upper bound that holds for

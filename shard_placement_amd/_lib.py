@@ -46,7 +46,8 @@ class TidePlanInfo(ctypes.Structure):
                 ("padded_numel", ctypes.c_int64), ("rs_tiles", ctypes.c_int64),
                 ("ag_tiles", ctypes.c_int64), ("rs_tile_elems", ctypes.c_int32),
                 ("ag_tile_elems", ctypes.c_int32), ("blob_bytes", ctypes.c_int64),
-                ("rs_launch_tiles", ctypes.c_int64), ("ag_launch_tiles", ctypes.c_int64)]
+                ("rs_launch_tiles", ctypes.c_int64), ("ag_launch_tiles", ctypes.c_int64),
+                ("rs_lds_bytes", ctypes.c_int64)]
 
 
 class TideError(RuntimeError):
@@ -122,8 +123,8 @@ def lib():
                  "tide_stream_create_cu_range", "tide_pipeline_create", "tide_pipeline_run",
                  "tide_pipeline_destroy"):
         getattr(L, name).restype = ctypes.c_int
-    if L.tide_abi_version() != 1:
-        raise RuntimeError("libtide ABI version %d, expected 1" % L.tide_abi_version())
+    if L.tide_abi_version() != 2:
+        raise RuntimeError("libtide ABI version %d, expected 2" % L.tide_abi_version())
     _lib = L
     return L
 

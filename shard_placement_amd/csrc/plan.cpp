@@ -48,13 +48,32 @@ constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 // never leaves); with launch boundaries the GEMM waits about half a launch.
 // Reduce-scatter: about 160 MiB of algorithmic traffic per launch (against
 // 256 MiB it halves the slowdown, +3..6% vs +9..13%, for 1-3% less
-// bandwidth; 128 MiB costs another 3%), but at least 1024 tiles (4
-// workgroups per CU: at R = 64 a 160 MiB launch holds only 620 tiles and
-// loses 7%).  Placement: 256 MiB (its own interference is not what the
+// bandwidth; 128 MiB costs another 3%).  A launch of fewer than 4
+// workgroups per CU is rounded down to whole workgroups per CU (256 tiles,
+// one per compute unit of the MI355X), and holds at least 2 per CU: at
+// R = 64 a 160 MiB launch would hold 620 tiles, 2.4 per CU, which leaves
+// the waves unbalanced (5.6 TB/s), while 512 tiles (132 MiB) read 6.01
+// TB/s against 6.12 at 1024 and cut the GEMM's slowdown from +12..14% to
+// +7..10%.  Placement: 256 MiB (its own interference is not what the
 // probe measures, and shorter launches cost it 4%).  An explicit launch
-// size applies to both.
+// size applies to both, unrounded.
+//
+// A launch of 2 workgroups per CU leaves room beside them (VGPRs, waves,
+// LDS) for a workgroup of a concurrent kernel, e.g. the single-wave GEMM's
+// (256 VGPRs per wave, 65 KB of LDS), which then shares the CU with
+// streaming reduce-scatter waves and finishes late.  (With 8 workgroups per
+// CU, as at R = 8, the wave slots are full and the GEMM waits for the
+// launch boundary instead.)  Such launches therefore hold 64 KB of LDS per
+// workgroup (the kernel uses 8 KB): two fill 128 of the CU's 160 KB, and a
+// workgroup needing more than 32 KB cannot start beside them.  Measured at
+// R = 64 (512 tiles per launch, 12 probes in 4 processes on one box): GEMM
+// slowdown +3.6..6.0% against +6.0..13.5% without the reservation (+11..15%
+// at 1024 tiles), reduce-scatter bandwidth unchanged (6.0 TB/s).
 constexpr int32_t kDefaultRsLaunchMiB = 160;
-constexpr int64_t kMinRsLaunchTiles = 1024;
+constexpr int64_t kCuTiles = 256;
+constexpr int64_t kRsRoundBelowTiles = 4 * kCuTiles;
+constexpr int64_t kMinRsLaunchTiles = 2 * kCuTiles;
+constexpr uint32_t kRsLdsReserve = 64 * 1024;
 constexpr int32_t kDefaultAgLaunchMiB = 256;
 
 struct Resolved {
@@ -64,6 +83,7 @@ struct Resolved {
     int64_t rs_launch_bytes;  // <= 0: unlimited
     int64_t ag_launch_bytes;
     int64_t rs_min_tiles;     // lower bound on tiles per reduce-scatter launch
+    bool rs_round;            // round short launches to whole workgroups per CU
 };
 
 tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
@@ -74,12 +94,14 @@ tide_status resolve_opts(const tide_opts* o, int32_t R, Resolved* out) {
     out->rs_launch_bytes = (int64_t)kDefaultRsLaunchMiB << 20;
     out->ag_launch_bytes = (int64_t)kDefaultAgLaunchMiB << 20;
     out->rs_min_tiles = kMinRsLaunchTiles;
+    out->rs_round = true;
     if (!o) return TIDE_OK;
     if (o->launch_mib < -1 || o->launch_mib > (1 << 20)) return TIDE_EINVAL;
     if (o->launch_mib != 0) {
         out->rs_launch_bytes = out->ag_launch_bytes =
             o->launch_mib == -1 ? 0 : (int64_t)o->launch_mib << 20;
         out->rs_min_tiles = 1;
+        out->rs_round = false;
     }
     if (o->align_elems < 1 || o->align_elems > (int64_t)1 << 20) return TIDE_EINVAL;
     out->align = o->align_elems;
@@ -445,10 +467,14 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     const int64_t ag_tile_bytes = (int64_t)o.ag_tile * 4;
     int64_t rs_launch = std::max<int64_t>(1, (int64_t)rs.size());
     int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
-    if (o.rs_launch_bytes > 0)
-        rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, o.rs_launch_bytes / rs_tile_bytes));
+    if (o.rs_launch_bytes > 0) {
+        int64_t t = o.rs_launch_bytes / rs_tile_bytes;
+        if (o.rs_round && t < kRsRoundBelowTiles) t = t / kCuTiles * kCuTiles;
+        rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));
+    }
     if (o.ag_launch_bytes > 0)
         ag_launch = std::min(ag_launch, std::max<int64_t>(1, o.ag_launch_bytes / ag_tile_bytes));
+    const uint32_t rs_lds = (o.rs_round && rs_launch <= kMinRsLaunchTiles) ? kRsLdsReserve : 0u;
     if (info) {
         std::memset(info, 0, sizeof(*info));
         info->R = R;
@@ -463,6 +489,7 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
         info->blob_bytes = (int64_t)L.bytes;
         info->rs_launch_tiles = rs_launch;
         info->ag_launch_tiles = ag_launch;
+        info->rs_lds_bytes = rs_lds ? rs_lds : kRsStaticLds;
     }
     if (blob_bytes < L.bytes) return TIDE_ENOSPACE;
 
@@ -495,6 +522,7 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     h.flags = o.flags;
     h.rs_launch_tiles = rs_launch;
     h.ag_launch_tiles = ag_launch;
+    h.rs_lds_bytes = rs_lds;
     std::memcpy(b, &h, sizeof h);
     if (P) std::memcpy(b + L.off_params, ps.data(), sizeof(ParamDesc) * (size_t)P);
     uint64_t* gp = reinterpret_cast<uint64_t*>(b + L.off_gptr);
@@ -531,6 +559,7 @@ tide_status tide_plan_query(const void* h_plan, tide_plan_info* info) {
     info->blob_bytes = (int64_t)h.bytes;
     info->rs_launch_tiles = h.rs_launch_tiles;
     info->ag_launch_tiles = h.ag_launch_tiles;
+    info->rs_lds_bytes = h.rs_lds_bytes ? h.rs_lds_bytes : kRsStaticLds;
     return TIDE_OK;
 }
 

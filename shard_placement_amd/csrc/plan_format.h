@@ -20,6 +20,7 @@ constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kVec = 8;            // bf16 elements per 16-byte vector
 constexpr int kTileQuantum = kBlock * kVec;  // tile sizes are multiples of this
 constexpr int kMaxRanks = 4096;
+constexpr int kRsStaticLds = kBlock * kVec * 4;  // the reduce-scatter kernels' store exchange
 
 // Plan-wide access hints; same values as TIDE_FLAG_* in tide.h.
 enum PlanFlags : uint32_t {
@@ -51,7 +52,7 @@ struct PlanHeader {
     int32_t has_rs;
     int32_t has_ag;
     uint32_t flags;
-    uint32_t reserved;
+    uint32_t rs_lds_bytes;    // LDS per reduce-scatter workgroup (0: the kernels' own)
     int64_t rs_launch_tiles;  // tiles per reduce-scatter kernel launch
     int64_t ag_launch_tiles;  // tiles per placement kernel launch
 };

@@ -649,6 +649,14 @@ FoldKernel pick_fold_tree(int R, uint32_t flags) {
 
 namespace {
 
+// Dynamic LDS a reduce-scatter launch requests on top of the kernel's own,
+// so that each workgroup holds the plan's LDS reservation (the kernels never
+// touch the extra bytes).
+static_assert(sizeof(float[kBlock * kVec]) == kRsStaticLds, "the kernels' static LDS");
+unsigned rs_extra_lds(const PlanHeader& h) {
+    return h.rs_lds_bytes > (uint32_t)kRsStaticLds ? h.rs_lds_bytes - (uint32_t)kRsStaticLds : 0u;
+}
+
 tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int64_t tile_begin,
                       int64_t tile_count, int32_t max_workgroups, tide_stream_t stream,
                       uint32_t* census = nullptr, int64_t census_len = 0) {
@@ -687,7 +695,8 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         uint32_t* cen = census ? census + (b - tile_begin) : nullptr;
         void* args[] = {&tiles, &ntiles, &gptr, &obase, &R, &cen};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
-                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+                                       dim3(kBlock), args, rs_extra_lds(h),
+                                       reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return TIDE_EHIP;
     }
     return TIDE_OK;
@@ -741,7 +750,8 @@ extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_pla
         if (grid > INT_MAX) grid = INT_MAX;
         void* args[] = {&tiles, &ntiles, &d_stage, &stride, &vec, &obase, &R};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
-                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+                                       dim3(kBlock), args, rs_extra_lds(h),
+                                       reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return TIDE_EHIP;
     }
     return TIDE_OK;
@@ -773,7 +783,8 @@ extern "C" tide_status tide_rs_tiles_to_stage(const void* h_plan, const void* d_
         float* out = stage + (b - tile_begin) * T;
         void* args[] = {&tiles, &ntiles, &gptr, &out, &T, &R};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
-                                       dim3(kBlock), args, 0, reinterpret_cast<hipStream_t>(stream));
+                                       dim3(kBlock), args, rs_extra_lds(h),
+                                       reinterpret_cast<hipStream_t>(stream));
         if (e != hipSuccess) return TIDE_EHIP;
     }
     return TIDE_OK;

@@ -106,6 +106,7 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
             out["modes"].append({
                 "mode": name, "max_workgroups": max_wg or None, "cu_mask": n_cu or None,
                 "tiles_per_launch": int(info.rs_launch_tiles),
+                "lds_per_workgroup": int(info.rs_lds_bytes),
                 "launches_per_rs": -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles))),
                 "rs_alone_ms": round(rs_alone, 4),
                 "rs_alone_gbps": round(rs_bytes / (rs_alone * 1e-3) / 1e9, 1),
@@ -150,3 +151,37 @@ def gemm_during(host_call, expect_ms: float, M: int = 4096, N: int = 4096, K: in
     return {"gemm_alone_ms": round(t0, 4), "gemm_during_staging_ms": round(t1, 4),
             "gemm_during_staging": n,
             "gemm_slowdown_during_staging_pct": round(100.0 * (t1 / t0 - 1.0), 2)}
+
+
+def main(argv=None) -> int:
+    """Standalone probe: set up one layer (reduce-scatter buffers only) and
+    run the default-launch probe ``--reps`` times in this process; prints
+    one JSON line {"workload": ..., "probe": {...}} with every repetition."""
+    import argparse
+    import json
+
+    from . import configs, harness
+
+    ap = argparse.ArgumentParser(description=main.__doc__)
+    ap.add_argument("--workload", default="5", help="workload key or name")
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--iters", type=int, default=40)
+    a = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        raise SystemExit("the probe needs a GPU")
+    w = configs.get(a.workload)
+    st = harness.setup(w, with_ag=False)
+    torch.cuda.synchronize()
+    res = None
+    for _ in range(a.reps):
+        r = run([("default launches", st.plan, 0, 0)], harness.rs_bytes(w), iters=a.iters)
+        if res is None:
+            res = r
+        else:
+            res["modes"] += r["modes"]
+    print(json.dumps({"workload": w.name, "R": w.R, "probe": res}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

@@ -55,7 +55,7 @@ def test_library_loads_and_exports_header_symbols():
     for name in declared:
         assert hasattr(L, name)
         assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
-    assert L.tide_abi_version() == 1
+    assert L.tide_abi_version() == 2
     assert L.tide_status_str(-3).decode().startswith("an output range overlaps")
 
 
@@ -291,21 +291,49 @@ def test_launch_granularity():
     g, o, ga, f = _fake_ptrs(shapes, R, S)
     _, info = api.tide_desc_build(shapes, R, g, o, ga, f)
     per_tile = info.rs_tile_elems * (2 * R + 4)
-    # library defaults: 160 MiB (at least 1024 tiles) for the reduce-scatter,
-    # 256 MiB for the placement
-    assert info.rs_launch_tiles == min(info.rs_tiles, max(1024, (160 << 20) // per_tile))
+    # library defaults: 160 MiB for the reduce-scatter (at R = 8, 4096 tiles:
+    # no rounding), 256 MiB for the placement
+    assert (160 << 20) // per_tile >= 1024
+    assert info.rs_launch_tiles == min(info.rs_tiles, (160 << 20) // per_tile)
+    # 16 workgroups per CU: no LDS reservation (the kernels' own 8 KB)
+    assert info.rs_lds_bytes == 8192
     assert info.ag_launch_tiles == min(info.ag_tiles, (256 << 20) // (info.ag_tile_elems * 4))
     _, big = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=256)
     assert big.rs_launch_tiles == min(big.rs_tiles, (256 << 20) // per_tile)
     assert big.ag_launch_tiles == min(big.ag_tiles, (256 << 20) // (big.ag_tile_elems * 4))
-    # at R = 64 a 160 MiB launch would hold ~620 tiles: the floor of 1024 applies
-    R64 = 64
+    # below 4 workgroups per CU a default launch is rounded down to whole
+    # workgroups per CU (multiples of 256 tiles), at least 512 tiles: at
+    # R = 64 a 160 MiB launch would hold ~620 tiles -> 512; at R = 128,
+    # ~315 -> 512; an explicit launch size is not rounded
     shapes64 = [(8192, 8192)]
-    _, _, _, S64 = api.tide_desc_geometry(shapes64, R64)
-    g64, o64, _, _ = _fake_ptrs(shapes64, R64, S64)
-    _, i64 = api.tide_desc_build(shapes64, R64, g64, o64, None, None)
-    assert (160 << 20) // (i64.rs_tile_elems * (2 * R64 + 4)) < 1024
-    assert i64.rs_launch_tiles == min(i64.rs_tiles, 1024)
+    for R64, want in ((64, 512), (128, 512)):
+        _, _, _, S64 = api.tide_desc_geometry(shapes64, R64)
+        g64, o64, _, _ = _fake_ptrs(shapes64, R64, S64)
+        _, i64 = api.tide_desc_build(shapes64, R64, g64, o64, None, None)
+        per64 = i64.rs_tile_elems * (2 * R64 + 4)
+        assert (160 << 20) // per64 < 1024
+        assert i64.rs_launch_tiles == min(i64.rs_tiles, want)
+        # 2 workgroups per CU: each holds 64 KB of LDS
+        assert i64.rs_lds_bytes == 64 * 1024
+        _, x64 = api.tide_desc_build(shapes64, R64, g64, o64, None, None, launch_mib=160)
+        assert x64.rs_launch_tiles == min(x64.rs_tiles, (160 << 20) // per64)
+        assert x64.rs_lds_bytes == 8192
+    # R = 32: ~1204 tiles per 160 MiB launch, 4.7 per CU, left as is
+    _, _, _, S32 = api.tide_desc_geometry(shapes64, 32)
+    g32, o32, _, _ = _fake_ptrs(shapes64, 32, S32)
+    _, i32 = api.tide_desc_build(shapes64, 32, g32, o32, None, None)
+    assert i32.rs_launch_tiles == (160 << 20) // (i32.rs_tile_elems * (2 * 32 + 4))
+    assert i32.rs_lds_bytes == 8192
+    # a layer of at most 512 tiles is one launch of at most 2 workgroups per
+    # CU: reserved too; the host blob carries it and tide_plan_query reads it
+    for Rs in (4, 17):
+        _, _, _, Ss = api.tide_desc_geometry([(64, 64)], Rs)
+        gs, os_, _, _ = _fake_ptrs([(64, 64)], Rs, Ss)
+        blob, tiny = api.tide_desc_build([(64, 64)], Rs, gs, os_, None, None)
+        assert tiny.rs_launch_tiles == tiny.rs_tiles <= 512 and tiny.rs_lds_bytes == 64 * 1024
+        q = _lib.TidePlanInfo()
+        assert _lib.lib().tide_plan_query(blob.ctypes.data, ctypes.byref(q)) == 0
+        assert q.rs_lds_bytes == 64 * 1024 and q.rs_launch_tiles == tiny.rs_launch_tiles
     _, one = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=-1)
     assert one.rs_launch_tiles == one.rs_tiles and one.ag_launch_tiles == one.ag_tiles
     _, small = api.tide_desc_build(shapes, R, g, o, ga, f, launch_mib=1)

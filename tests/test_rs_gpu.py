@@ -264,6 +264,33 @@ def test_launch_size_same_bits(launch_mib):
     gu.check_ag_full(st)
 
 
+@pytest.mark.parametrize("order", ["fixed", "tree"])
+@pytest.mark.parametrize("max_wg", [0, 3])
+def test_lds_reserving_launches_same_bits(order, max_wg):
+    """At R = 64 the default launches hold 512 tiles and each workgroup
+    holds 64 KB of LDS (56 KB of it requested at launch, never touched).
+    The bits are the oracle's and those of one launch without the
+    reservation: 2241 tiles make four full launches and one of 193; with a
+    capped grid each workgroup strides over tiles."""
+    w = _wl([(1001, 64), (128,), (3, 8), (8192, 512)], 64, key=171, sigma=1e-3)
+    gu.say("lds-reserving rs", order, "max_wg", max_wg)
+    st = harness.setup(w, with_ag=False)
+    info = st.plan.info
+    assert info.rs_lds_bytes == 64 * 1024
+    assert (info.rs_tiles, info.rs_launch_tiles) == (2241, 512)
+    _run(st, order, max_wg)
+    gu.check_rs_full(st, order)
+    got = [o.clone() for o in st.out]
+    one = api.Plan(w.shapes, w.R, grads=st.grads, out=st.out, launch_mib=-1)
+    assert one.info.rs_lds_bytes == 8192
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    one.rs(order=order)
+    torch.cuda.synchronize()
+    for a, b in zip(got, st.out):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_hip_graph_replays_match_eager():
     """One step (placement + reduce-scatter, several launches each) captured
     in a HIP graph: every replay, with eager work and synchronisation in
