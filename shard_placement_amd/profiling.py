@@ -6,12 +6,15 @@ WRITE_SIZE, scaled by the same counters read on a plain copy of known size).
     python -m shard_placement_amd.profiling pmc FETCH_DIR WRITE_DIR OUT.txt \
         --kernel rs_fixed_kernel --calib-kernel copy --calib-bytes N \
         --algorithmic-bytes B --src-hash H --command "..."
+    python -m shard_placement_amd.profiling overlap OUT.txt --dirs D1 D2 \
+        --logs L1 L2 --command "..." --title "..."
 """
 from __future__ import annotations
 
 import argparse
 import csv
 import glob
+import json
 import os
 import statistics
 import sys
@@ -65,6 +68,78 @@ def summarize_stats(d: str, out: str, command: str, top: int = 12) -> None:
                 t.get("Scratch_Size", "?")))
     except FileNotFoundError:
         pass
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _med(xs):
+    return statistics.median(xs) if xs else float("nan")
+
+
+def overlap_of(d: str, gemm_substr: str = "Cijk", rs_substr: str = "rs_fixed_kernel") -> dict:
+    """From one process's kernel trace: the GEMMs that overlap at least one
+    reduce-scatter launch, their durations, how many launches overlap each
+    and how many launch ends fall inside each, the durations of the launches
+    that overlap a GEMM and of those that do not (microseconds)."""
+    tr = kernel_trace(d)
+    span = lambda t: (int(t["Start_Timestamp"]), int(t["End_Timestamp"]))
+    gemms = sorted(span(t) for t in tr if gemm_substr in t.get("Kernel_Name", ""))
+    rs = sorted(span(t) for t in tr if rs_substr in t.get("Kernel_Name", ""))
+    dur, n_ov, n_end, rs_ov = [], [], [], set()
+    for a, b in gemms:
+        ov = [i for i, (s, e) in enumerate(rs) if s < b and e > a]
+        if not ov:
+            continue
+        dur.append((b - a) / 1e3)
+        n_ov.append(len(ov))
+        n_end.append(sum(1 for i in ov if a < rs[i][1] < b))
+        rs_ov.update(ov)
+    rs_ov_d = [(rs[i][1] - rs[i][0]) / 1e3 for i in sorted(rs_ov)]
+    rs_free_d = [(e - s) / 1e3 for i, (s, e) in enumerate(rs) if i not in rs_ov]
+    return {"gemms": len(dur), "gemm_us": dur, "launches_per_gemm": n_ov,
+            "ends_inside": n_end, "rs_overlapping_us": rs_ov_d, "rs_alone_us": rs_free_d}
+
+
+def summarize_overlap(dirs, logs, out: str, command: str, title: str) -> None:
+    """One block per process: the probe's own results (the JSON line that
+    bench.py or the standalone probe printed in that process) and the
+    overlap figures from its kernel trace."""
+    lines = ["# rocprofv3 kernel trace of the default-configuration interference probe, %s" % title,
+             "command (one process each): %s" % command,
+             "per process: the probe's result line, then over the GEMMs (Cijk_* kernels) that overlap",
+             "at least one reduce-scatter launch (rs_fixed_kernel): GEMM duration, launches overlapping",
+             "each GEMM, launch ends inside each GEMM, and the duration of the launches that overlap a",
+             "GEMM against those that do not"]
+    for i, (d, lg) in enumerate(zip(dirs, logs), 1):
+        probe = None
+        with open(lg) as fh:
+            for line in fh:
+                if line.startswith("{"):
+                    probe = json.loads(line).get("probe")
+        o = overlap_of(d)
+        lines.append("")
+        modes = (probe or {}).get("modes") or []
+        for j, m in enumerate(modes):
+            lines.append("process %d%s: probe (%s, %s tiles per launch, %s B of LDS per workgroup): RS "
+                         "alone %.1f GB/s, beside the GEMM %.1f GB/s; GEMM %.4f -> %s ms (%s%%, %d GEMMs "
+                         "inside)" % (
+                             i, "" if len(modes) == 1 else " run %d" % (j + 1), m["mode"],
+                             m["tiles_per_launch"], m.get("lds_per_workgroup", "?"),
+                             m["rs_alone_gbps"],
+                             m["rs_concurrent_gbps"], m["t_gemm_alone_ms"],
+                             m["t_gemm_concurrent_ms"], m["gemm_slowdown_pct"], m["gemm_inside"]))
+        if not o["gemms"]:
+            lines.append("  no GEMM overlaps a reduce-scatter launch")
+            continue
+        lines.append("  GEMMs overlapping the RS: %d; duration median %.0f us (min %.0f, max %.0f)" % (
+            o["gemms"], _med(o["gemm_us"]), min(o["gemm_us"]), max(o["gemm_us"])))
+        lines.append("  RS launches overlapping each GEMM: median %g (min %d, max %d); launch ends inside "
+                     "a GEMM: median %g" % (_med(o["launches_per_gemm"]), min(o["launches_per_gemm"]),
+                                            max(o["launches_per_gemm"]), _med(o["ends_inside"])))
+        lines.append("  RS launches overlapping a GEMM: %d, duration median %.0f us (max %.0f); the other "
+                     "%d: median %.1f us" % (len(o["rs_overlapping_us"]), _med(o["rs_overlapping_us"]),
+                                             max(o["rs_overlapping_us"]), len(o["rs_alone_us"]),
+                                             _med(o["rs_alone_us"])))
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -140,9 +215,19 @@ def main(argv=None):
     p.add_argument("--workload", required=True)
     p.add_argument("--command-fetch", required=True)
     p.add_argument("--command-write", required=True)
+    o = sub.add_parser("overlap")
+    o.add_argument("out")
+    o.add_argument("--dirs", nargs="+", required=True, help="kernel-trace folders, one per process")
+    o.add_argument("--logs", nargs="+", required=True, help="bench.py output of the same processes")
+    o.add_argument("--command", required=True)
+    o.add_argument("--title", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         summarize_stats(a.dir, a.out, a.command)
+    elif a.cmd == "overlap":
+        if len(a.dirs) != len(a.logs):
+            raise SystemExit("--dirs and --logs must pair up")
+        summarize_overlap(a.dirs, a.logs, a.out, a.command, a.title)
     else:
         summarize_pmc(a.fetch_dir, a.write_dir, a.out, a.kernel, a.calib_kernel, a.calib_bytes,
                       a.algorithmic_bytes, a.src_hash, a.command_fetch, a.command_write, a.workload)
