@@ -66,9 +66,10 @@ constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 // launch boundary instead.)  Such launches therefore hold 64 KB of LDS per
 // workgroup (the kernel uses 8 KB): two fill 128 of the CU's 160 KB, and a
 // workgroup needing more than 32 KB cannot start beside them.  Measured at
-// R = 64 (512 tiles per launch, 12 probes in 4 processes on one box): GEMM
-// slowdown +3.6..6.0% against +6.0..13.5% without the reservation (+11..15%
-// at 1024 tiles), reduce-scatter bandwidth unchanged (6.0 TB/s).
+// R = 64 (512 tiles per launch, two boxes, 4 processes each): GEMM slowdown
+// +2.3..6.5% (mean 5.0 and 4.8%) against +2.9..9.4% (mean 6.0 and 7.3%)
+// without the reservation and +11..15% at 1024 tiles; reduce-scatter
+// bandwidth unchanged (6.0 TB/s).
 constexpr int32_t kDefaultRsLaunchMiB = 160;
 constexpr int64_t kCuTiles = 256;
 constexpr int64_t kRsRoundBelowTiles = 4 * kCuTiles;

@@ -15,6 +15,8 @@ rocprofv3 kernel trace).  It is a measurement: nothing here is parity.
 """
 from __future__ import annotations
 
+import contextlib
+import gc
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
@@ -30,6 +32,23 @@ def _median(xs: List[float]) -> Optional[float]:
         return None
     xs = sorted(xs)
     return xs[len(xs) // 2]
+
+
+@contextlib.contextmanager
+def _no_gc():
+    """The Python garbage collector paused (after one collection), as
+    Python's timeit does while timing.  Measured on the R = 64 layer: a
+    collection pass inside the concurrent window read +17..23% GEMM slowdown
+    where the same process with the collector paused, or collected just
+    before, read +2..7%."""
+    was = gc.isenabled()
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
 
 
 def _gemm_train(a, b, c, stream, n):
@@ -51,7 +70,12 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
     reduce-scatter always runs on a CU-masked stream, which HIP backs with a
     hardware queue of its own (with the full mask when the mode has none):
     two streams that share a hardware queue run one after the other, which
-    would hide any interference."""
+    would hide any interference.  The garbage collector is paused meanwhile."""
+    with _no_gc():
+        return _run(modes, rs_bytes, iters, M, N, K)
+
+
+def _run(modes, rs_bytes, iters, M, N, K) -> Dict:
     dev = torch.device("cuda")
     n_all = torch.cuda.get_device_properties(dev).multi_processor_count
     a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
@@ -124,6 +148,11 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
 
 
 def gemm_during(host_call, expect_ms: float, M: int = 4096, N: int = 4096, K: int = 8192) -> Dict:
+    with _no_gc():
+        return _gemm_during(host_call, expect_ms, M, N, K)
+
+
+def _gemm_during(host_call, expect_ms, M, N, K) -> Dict:
     """Median time of the single-wave GEMM alone (trains before and after,
     pooled), and while ``host_call`` (a host-synchronous call that keeps the
     DMA engines busy for about expect_ms, e.g. copy-engine staging) runs: a
