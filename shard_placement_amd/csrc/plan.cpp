@@ -53,8 +53,8 @@ constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 // one per compute unit of the MI355X), and holds at least 2 per CU: at
 // R = 64 a 160 MiB launch would hold 620 tiles, 2.4 per CU, which leaves
 // the waves unbalanced (5.6 TB/s), while 512 tiles (132 MiB) read 6.01
-// TB/s against 6.12 at 1024 and cut the GEMM's slowdown from +12..14% to
-// +7..10%.  Placement: 256 MiB (its own interference is not what the
+// TB/s against 6.12 at 1024 and cut the GEMM's slowdown from +11..15% to
+// +3..10%.  Placement: 256 MiB (its own interference is not what the
 // probe measures, and shorter launches cost it 4%).  An explicit launch
 // size applies to both, unrounded.
 //
