@@ -318,6 +318,12 @@ def test_launch_granularity():
         _, x64 = api.tide_desc_build(shapes64, R64, g64, o64, None, None, launch_mib=160)
         assert x64.rs_launch_tiles == min(x64.rs_tiles, (160 << 20) // per64)
         assert x64.rs_lds_bytes == 8192
+    # R = 40: ~975 tiles -> 768 (3 per CU): rounded, not reserved
+    _, _, _, S40 = api.tide_desc_geometry(shapes64, 40)
+    g40, o40, _, _ = _fake_ptrs(shapes64, 40, S40)
+    _, i40 = api.tide_desc_build(shapes64, 40, g40, o40, None, None)
+    assert (160 << 20) // (i40.rs_tile_elems * (2 * 40 + 4)) == 975
+    assert i40.rs_launch_tiles == 768 and i40.rs_lds_bytes == 8192
     # R = 32: ~1204 tiles per 160 MiB launch, 4.7 per CU, left as is
     _, _, _, S32 = api.tide_desc_geometry(shapes64, 32)
     g32, o32, _, _ = _fake_ptrs(shapes64, 32, S32)
