@@ -19,6 +19,7 @@ configuration (--probe adds other launch sizes, grid caps and CU masks).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -441,6 +442,13 @@ def main():
         del src, dst
 
     rsb, agb = harness.rs_bytes(w), harness.ag_bytes(w)
+
+    # Python's garbage collector stays paused from here on, as timeit does
+    # while timing: a collection pass inside a timed region once read as a
+    # +17..23% GEMM slowdown in the interference probe, and the host-timed
+    # legs (copy engines, pipeline issue) would absorb its pauses too.
+    gc.collect()
+    gc.disable()
 
     def step(ev=None):
         if ev:
