@@ -22,3 +22,13 @@ def test_timed_regions_pause_the_garbage_collector():
         assert not gc.isenabled()  # left as the caller had it
     finally:
         gc.enable()
+
+
+def test_standalone_probe_needs_a_gpu():
+    import pytest
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(SystemExit, match="needs a GPU"):
+        probe.main(["--workload", "1"])
