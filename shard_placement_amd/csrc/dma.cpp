@@ -278,13 +278,11 @@ tide_status check_pipeline(const void* h_plan, const void* d_plan, int64_t tile_
 
 }  // namespace tide
 
-extern "C" tide_status tide_rs_stage_to_shards_sdma(const void* h_plan, int64_t tile_begin,
-                                                    int64_t tile_count, const float* stage,
-                                                    int64_t stage_elems, tide_stream_t stream) {
-    PlanHeader h;
-    tide_status st = check_pipeline(h_plan, nullptr, tile_begin, tile_count, stage, stage_elems, 0,
-                                    &h);
-    if (st != TIDE_OK) return st;
+namespace tide {
+
+tide_status issue_stage_to_shards_sdma(const PlanHeader& h, const void* h_plan,
+                                       int64_t tile_begin, int64_t tile_count, const float* stage,
+                                       tide_stream_t stream) {
     const uint8_t* b = static_cast<const uint8_t*>(h_plan);
     const RsTile* tiles = reinterpret_cast<const RsTile*>(b + h.off_rs);
     const uint64_t* obase = reinterpret_cast<const uint64_t*>(b + h.off_obase);
@@ -313,6 +311,18 @@ extern "C" tide_status tide_rs_stage_to_shards_sdma(const void* h_plan, int64_t 
         t = u;
     }
     return TIDE_OK;
+}
+
+}  // namespace tide
+
+extern "C" tide_status tide_rs_stage_to_shards_sdma(const void* h_plan, int64_t tile_begin,
+                                                    int64_t tile_count, const float* stage,
+                                                    int64_t stage_elems, tide_stream_t stream) {
+    PlanHeader h;
+    tide_status st = check_pipeline(h_plan, nullptr, tile_begin, tile_count, stage, stage_elems, 0,
+                                    &h);
+    if (st != TIDE_OK) return st;
+    return issue_stage_to_shards_sdma(h, h_plan, tile_begin, tile_count, stage, stream);
 }
 
 extern "C" tide_status tide_dma_engine_count(int32_t* count) {

@@ -192,15 +192,16 @@ extern "C" tide_status tide_pipeline_run(tide_pipeline_t p, const void* h_plan,
             st = TIDE_EHIP;
             break;
         }
-        st = tide_rs_tiles_to_stage(h_plan, d_plan, b, cnt, buf, slot, 0, s1);
+        // the ring and the tile range were checked above, once for all chunks
+        st = issue_tiles_to_stage(h, d_plan, b, cnt, buf, 0, s1);
         if (st != TIDE_OK) break;
         if (hipEventRecord(p->produced[k], p->s1) != hipSuccess ||
             hipStreamWaitEvent(p->s2, p->produced[k], 0) != hipSuccess) {
             st = TIDE_EHIP;
             break;
         }
-        st = phase2 == 0 ? tide_rs_stage_to_shards(h_plan, d_plan, b, cnt, buf, slot, 0, s2)
-                         : tide_rs_stage_to_shards_sdma(h_plan, b, cnt, buf, slot, s2);
+        st = phase2 == 0 ? issue_stage_to_shards(h, d_plan, b, cnt, buf, 0, s2)
+                         : issue_stage_to_shards_sdma(h, h_plan, b, cnt, buf, s2);
         if (st != TIDE_OK) break;
         if (hipEventRecord(p->drained[k], p->s2) != hipSuccess) st = TIDE_EHIP;
     }

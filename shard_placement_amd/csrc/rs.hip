@@ -757,15 +757,11 @@ extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_pla
     return TIDE_OK;
 }
 
-extern "C" tide_status tide_rs_tiles_to_stage(const void* h_plan, const void* d_plan,
-                                              int64_t tile_begin, int64_t tile_count,
-                                              float* stage, int64_t stage_elems,
-                                              int32_t max_workgroups, tide_stream_t stream) {
-    if (!d_plan) return TIDE_EINVAL;
-    PlanHeader h;
-    tide_status st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, stage_elems,
-                                    max_workgroups, &h);
-    if (st != TIDE_OK) return st;
+namespace tide {
+
+tide_status issue_tiles_to_stage(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
+                                 int64_t tile_count, float* stage, int32_t max_workgroups,
+                                 tide_stream_t stream) {
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
     const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
@@ -790,15 +786,9 @@ extern "C" tide_status tide_rs_tiles_to_stage(const void* h_plan, const void* d_
     return TIDE_OK;
 }
 
-extern "C" tide_status tide_rs_stage_to_shards(const void* h_plan, const void* d_plan,
-                                               int64_t tile_begin, int64_t tile_count,
-                                               const float* stage, int64_t stage_elems,
-                                               int32_t max_workgroups, tide_stream_t stream) {
-    if (!d_plan) return TIDE_EINVAL;
-    PlanHeader h;
-    tide_status st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, stage_elems,
-                                    max_workgroups, &h);
-    if (st != TIDE_OK) return st;
+tide_status issue_stage_to_shards(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
+                                  int64_t tile_count, const float* stage, int32_t max_workgroups,
+                                  tide_stream_t stream) {
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
     const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
     const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
@@ -824,6 +814,32 @@ extern "C" tide_status tide_rs_stage_to_shards(const void* h_plan, const void* d
         if (e != hipSuccess) return TIDE_EHIP;
     }
     return TIDE_OK;
+}
+
+}  // namespace tide
+
+extern "C" tide_status tide_rs_tiles_to_stage(const void* h_plan, const void* d_plan,
+                                              int64_t tile_begin, int64_t tile_count,
+                                              float* stage, int64_t stage_elems,
+                                              int32_t max_workgroups, tide_stream_t stream) {
+    if (!d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    tide_status st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, stage_elems,
+                                    max_workgroups, &h);
+    if (st != TIDE_OK) return st;
+    return issue_tiles_to_stage(h, d_plan, tile_begin, tile_count, stage, max_workgroups, stream);
+}
+
+extern "C" tide_status tide_rs_stage_to_shards(const void* h_plan, const void* d_plan,
+                                               int64_t tile_begin, int64_t tile_count,
+                                               const float* stage, int64_t stage_elems,
+                                               int32_t max_workgroups, tide_stream_t stream) {
+    if (!d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    tide_status st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, stage_elems,
+                                    max_workgroups, &h);
+    if (st != TIDE_OK) return st;
+    return issue_stage_to_shards(h, d_plan, tile_begin, tile_count, stage, max_workgroups, stream);
 }
 
 extern "C" tide_status tide_rs_bf16_to_fp32_census(const void* h_plan, const void* d_plan,

@@ -33,4 +33,18 @@ tide_status check_pipeline(const void* h_plan, const void* d_plan, int64_t tile_
                            int64_t tile_count, const float* stage, int64_t stage_elems,
                            int32_t max_workgroups, PlanHeader* h);
 
+// The two phases' launches and copies, without the checks: for callers that
+// have validated the plan, the tile range and the staging memory already
+// (the pipeline driver checks its whole ring once, then issues chunk by
+// chunk).  h is the plan's header.
+tide_status issue_tiles_to_stage(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
+                                 int64_t tile_count, float* stage, int32_t max_workgroups,
+                                 tide_stream_t stream);
+tide_status issue_stage_to_shards(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
+                                  int64_t tile_count, const float* stage, int32_t max_workgroups,
+                                  tide_stream_t stream);
+tide_status issue_stage_to_shards_sdma(const PlanHeader& h, const void* h_plan,
+                                       int64_t tile_begin, int64_t tile_count, const float* stage,
+                                       tide_stream_t stream);
+
 }  // namespace tide
