@@ -18,12 +18,12 @@
  *
  *   reduce-scatter  R ranks' per-parameter bf16 gradients, read in place,
  *                   are reduced into each rank's fp32 dim-0 shards
- *                   [Abstract: "consumes per-parameter bf16 gradients
- *                   directly and reduces them into fp32 shards"];
+ *                   [Abstract: TIDE-RS takes the bf16 gradient tensors
+ *                   as they are and produces fp32 shards];
  *   AG placement    a rank-major bf16 gathered buffer [Root] is written
  *                   straight into the per-parameter full tensors, the
- *                   padding rows trimmed [Abstract: TIDE-AG "delivers shards
- *                   directly to parameter storage"].
+ *                   padding rows trimmed [Abstract: TIDE-AG puts shards
+ *                   into the parameters' own storage].
  *
  * Layout conventions (the pages leave them open; these readings are the
  * library's contract):
@@ -132,8 +132,8 @@ typedef struct tide_plan_info {
 } tide_plan_info;
 
 /* Size of the plan blob for these shapes (an upper bound that holds for
- * any pointers).  shapes: P entries, host memory.  [Abstract: layout
- * placement folded into collective addressing] */
+ * any pointers).  shapes: P entries, host memory.  [Abstract: the
+ * parameter layout becomes part of the collectives' addressing] */
 tide_status tide_desc_size(const tide_shape *shapes, int32_t P, int32_t R,
                            const tide_opts *opts, size_t *blob_bytes);
 
@@ -194,12 +194,14 @@ tide_status tide_rs_bf16_to_fp32(const void *h_plan, const void *d_plan,
                                  tide_stream_t stream);
 
 /* The same reduce-scatter restricted to tiles [tile_begin, tile_begin +
- * tile_count) of the plan (tide_plan_info.rs_tiles in all; tiles are in
- * parameter order, then rank, then flat index).  Lets a caller cut one
+ * tile_count) of the plan (tide_plan_info.rs_tiles in all; tiles are listed
+ * by output rank, then parameter, then flat index, so rank r's tiles are the
+ * one range tide_plan_rank_tiles returns).  Lets a caller cut one
  * layer's reduce-scatter into several short launches, e.g. to leave the
  * compute units to concurrent work between them, or to pipeline the
- * gradient reads with a consumer of finished tiles [Abstract: a two-phase
- * pipeline separates gradient reads from network progress].  A range past
+ * gradient reads with a consumer of finished tiles [Abstract: the
+ * reduce-scatter runs as two pipelined phases, reading gradients apart from
+ * moving results over the network].  A range past
  * the end is TIDE_EINVAL; tile_count == 0 launches nothing. */
 tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
                                        int32_t order, int64_t tile_begin,
@@ -226,7 +228,7 @@ tide_status tide_ag_place(const void *h_plan, const void *d_plan,
                           int32_t max_workgroups, tide_stream_t stream);
 
 /* The same placement issued as host-side copies from the host plan,
- * asynchronous on `stream` [Abstract: no SMs used for placement].
+ * asynchronous on `stream` [Abstract: placement without compute units].
  * engine_only = 1: one 1-D copy per (param, rank) run with the runtime's
  * no-compute-unit copy kind (hipMemcpyDeviceToDeviceNoCU); the runtime
  * picks the engine: usually the DMA engines, but it has also been seen to
@@ -249,7 +251,8 @@ tide_status tide_ag_place_sdma_streams(const void *h_plan, const tide_stream_t *
 /* The same placement on the DMA copy engines, issued through ROCr: one 1-D
  * copy per (param, rank) run, each pinned to one engine, spread over all
  * the device's engines (largest first, each to the engine with the fewest
- * bytes so far) [Abstract: no SMs used for transport or placement].
+ * bytes so far) [Abstract: transport and placement kept off the compute
+ * units].
  * Host-synchronous: waits for `stream` to finish its earlier work, then
  * returns when every copy has completed (no kernel runs).  Do not overlap
  * it with the runtime's own copy-engine copies (tide_ag_place_sdma, D2H
@@ -261,8 +264,8 @@ tide_status tide_ag_place_dma(const void *h_plan, tide_stream_t stream);
  * the current device (*count = 0 and TIDE_EUNSUPPORTED if none). */
 tide_status tide_dma_engine_count(int32_t *count);
 
-/* Copy-engine-staged reduce-scatter [Abstract: copy engines and short-lived
- * thread blocks; Design], in two calls.
+/* Copy-engine-staged reduce-scatter [Abstract: data movement on the copy
+ * engines, the sums in brief thread blocks; Design], in two calls.
  *
  * Staging buffers: h_stage[r] (host array of R device addresses) is rank
  * r's staging buffer of R slots of bf16; slot q starts slot_stride elements

@@ -10,16 +10,17 @@
  * Sources (cited by page and section, never by line):
  *   [Abstract]   "The Endgame of FSDP Communication: Layout-Aware Collectives
  *                on Copy Engines, RDMA, and NVSwitch" (weekinpapers.com),
- *                section Abstract.  FSDP2 keeps per-parameter gradient
- *                tensors; TIDE-RS consumes the per-parameter bf16 gradients
- *                directly and reduces them into fp32 shards; TIDE-AG delivers
- *                shards directly into parameter storage.
+ *                section Abstract.  FSDP2 keeps one gradient tensor per
+ *                parameter; TIDE-RS reads those bf16 tensors where they lie
+ *                and sums them into fp32 shards; TIDE-AG writes shards into
+ *                the parameters' own storage without a copy-out pass.
  *   [Root]       kongchang.com article "The Endgame of FSDP Communication:
  *                TIDE Zero-Copy Collective Communication Optimization",
  *                section "The Root of FSDP2 Communication Overhead": the
  *                rank-major buffer (each rank's block contiguous, blocks in
- *                rank order) and reduce-scatter semantics (every rank holds a
- *                full buffer and ends with the reduction of its own shard).
+ *                rank order) and what a reduce-scatter does (each rank
+ *                starts from a whole buffer and keeps only the sum of its
+ *                own shard).
  *
  * Readings taken where the pages are silent (each is also listed with its
  * reason in the design notes):

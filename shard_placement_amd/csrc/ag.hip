@@ -1,10 +1,11 @@
 // ag.hip -- all-gather placement for gfx950: rank-major bf16 gathered
 // buffer -> per-parameter full tensors, padding rows trimmed.
 //
-// TIDE-AG "delivers shards directly to parameter storage" (Abstract of "The
-// Endgame of FSDP Communication", weekinpapers.com); the gathered buffer is
-// rank-major: each rank's block contiguous, blocks in rank order (kongchang.com
-// article, section "The Root of FSDP2 Communication Overhead").  On one GPU
+// TIDE-AG writes each rank's shard straight into the parameter's own tensor,
+// with no separate copy-out pass (Abstract of "The Endgame of FSDP
+// Communication", weekinpapers.com); the gathered buffer is rank-major: each
+// rank's block contiguous, blocks in rank order (kongchang.com article,
+// section "The Root of FSDP2 Communication Overhead").  On one GPU
 // the delivery is the placement step itself: for param p and rank r the
 // clamp(d0 - r*s, 0, s) valid rows of slot r land in rows [r*s, ...) of the
 // full tensor; slot padding is never read.
@@ -17,8 +18,8 @@
 //                       lane), 4-byte or 2-byte moves otherwise.
 //   tide_ag_place_sdma  host-issued copies.  engine_only = 1: one 1-D copy
 //                       per (param, rank) run with the no-compute-unit copy
-//                       kind, executed by the DMA engines ("no SMs used for
-//                       transport or placement", same Abstract).
+//                       kind, executed by the DMA engines (the pages move and
+//                       place data without compute units, same Abstract).
 //                       engine_only = 0: one 2-D copy per param over the
 //                       ranks whose shard is full plus a 1-D copy for the
 //                       partial rank, which the runtime executes with a

@@ -1,10 +1,11 @@
 // dma.cpp -- data movement on the DMA (SDMA) copy engines, issued through
 // ROCr, for the two places where the pages move data without compute units:
-// placement of all-gather outputs into parameter storage, and staging of
-// gradients before a short-lived reduction ("copy engines and short-lived
-// thread blocks", "no SMs used for transport or placement", Abstract of "The
-// Endgame of FSDP Communication", weekinpapers.com; "TIDE's Design
-// Approach" of the kongchang.com article).
+// putting gathered shards into the parameter tensors, and staging gradients
+// for a reduction that only brief compute work performs (the pages split the
+// work between the copy engines and brief thread blocks, and keep the
+// compute units out of transport and placement: Abstract of "The Endgame of
+// FSDP Communication", weekinpapers.com; "TIDE's Design Approach" of the
+// kongchang.com article).
 //
 // Every copy is a 1-D copy pinned to one engine; one call spreads its
 // copies over all engines the device offers (largest first, each to the

@@ -1,9 +1,9 @@
 // plan.cpp -- host side of libtide: plan (descriptor table) builder,
 // validation and status strings.  Pure host C++; no HIP call is made here.
 //
-// The plan folds the FSDP2 layout into the kernels' addressing (Abstract of
-// "The Endgame of FSDP Communication", weekinpapers.com: "folding layout
-// placement into collective addressing"): per parameter it records the
+// The plan makes the FSDP2 layout part of the kernels' addressing (Abstract
+// of "The Endgame of FSDP Communication", weekinpapers.com): per parameter
+// it records the
 // shard geometry, per (rank, parameter) the gradient pointer, and it cuts
 // every rank's shard into tiles that a workgroup can process without any
 // further layout arithmetic.  Shard geometry follows the library contract

@@ -1,8 +1,8 @@
 // plan_format.h -- in-memory layout of a libtide plan blob (host and device).
 //
-// The plan is the descriptor table that folds the layout into the kernels'
-// addressing ("folding layout placement into collective addressing",
-// Abstract of "The Endgame of FSDP Communication", weekinpapers.com).  It is
+// The plan is the descriptor table through which the parameter layout
+// becomes part of the kernels' addressing, the central idea of the Abstract
+// of "The Endgame of FSDP Communication" (weekinpapers.com).  It is
 // built on the host once per layer (plan.cpp), uploaded by the caller, and
 // read by the kernels: every workgroup looks up one tile and from it the
 // per-rank source pointers and the destination pointer of its run.

@@ -1,9 +1,10 @@
 // rs.hip -- fused bf16 -> fp32 dim-0-shard reduce-scatter for gfx950.
 //
-// TIDE-RS "consumes per-parameter bf16 gradients directly and reduces them
-// into fp32 shards" (Abstract of "The Endgame of FSDP Communication",
-// weekinpapers.com); in a reduce-scatter every rank holds a full buffer and
-// ends with the reduction of its own shard (kongchang.com article, section
+// TIDE-RS reads each parameter's bf16 gradient tensor where it lies and
+// reduces it into fp32 shards (Abstract of "The Endgame of FSDP
+// Communication", weekinpapers.com); a reduce-scatter starts from one
+// whole buffer per rank and leaves each rank with the sum of its own shard
+// only (kongchang.com article, section
 // "The Root of FSDP2 Communication Overhead").  Here all R ranks' gradient
 // tensors sit in one GPU's HBM and are read in place: no rank-major pack
 // buffer, no fp32 staging copy.

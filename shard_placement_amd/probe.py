@@ -1,8 +1,9 @@
 """Interference probe: how much the reduce-scatter slows a concurrent GEMM.
 
-The paper reports that a default reduce-scatter can slow a concurrent GEMM
-that would otherwise finish in a single wave by 69%, and that TIDE cuts that
-interference by up to an order of magnitude (Abstract of "The Endgame of
+The paper measures a 69% slowdown of a concurrent GEMM (one that would fit
+in one wave of thread blocks on its own) caused by the default NCCL
+reduce-scatter, and reports that TIDE lowers that interference roughly
+tenfold (Abstract of "The Endgame of
 FSDP Communication", weekinpapers.com; kongchang.com article, sections "The
 Root of FSDP2 Communication Overhead" and "Performance").  This probe times a
 bf16 GEMM (torch.matmul -> hipBLASLt) alone, then beside a train of
