@@ -8,7 +8,13 @@ gradients into fp32 dim-0 shards (the plan is built once per layer, before
 timing, as in training).  Inputs are resident in HBM before the timed
 region.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--probe]
+    python bench.py [--steps K] [--warmup W] [--workload 5] [--probe]
+
+The default workload is the largest: one Llama-3.1-70B decoder layer plus a
+ragged [1001, 8192] param at R = 64, its fp32 shards staged in the vacated
+gathered buffers (Slot-Reuse), with the interference probe's single-wave
+GEMM beside the reduce-scatter.  The other layers (R = 8, 16, 32) get a
+compact record of their RS and AG rates at the end (--others).
 
 Metric (bytes are algorithmic): RS GB/s = (R*N*2 + N*4) / t_RS and its
 fraction of the 8 TB/s HBM peak; AG GB/s = 4*N / t_AG; GEMM slowdown of a
@@ -32,6 +38,23 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+# The pages' own figures, measured on NVIDIA clusters (context only: other
+# hardware, whole training steps, real networks).  Abstract of "The Endgame
+# of FSDP Communication" (weekinpapers.com); kongchang.com article, sections
+# "The Root of FSDP2 Communication Overhead" and "Performance: Step Time
+# Reduction and Interference Cut".
+PAGES_CONTEXT = {
+    "hardware": "NVIDIA GPUs with NCCL; the system results on 64 GPUs (NVSwitch + RDMA), "
+                "GPU count not stated for the two overhead figures",
+    "layout_conversion_pct_of_step": 6.4,
+    "layout_conversion_workload": "Llama-3.1 70B, 8K tokens per GPU",
+    "gemm_slowdown_from_default_rs_pct": 69,
+    "rs_sm_time_reduction_x": [12.5, 14.5],
+    "interference_reduction": "up to about 10x",
+    "step_time_reduction_pct": {"vs_stock_fsdp2": 27.1, "vs_fsdp2_symmmem": 6.0},
+}
+
 PROFILES = os.path.join(HERE, "profiles")
 # what decides a kernel's launches: its source, the shared headers, and the
 # plan builder (tile sizes, order, kinds)
@@ -305,75 +328,117 @@ def stock_leg(st, rsb: int, agb: int, reps: int = 3) -> dict:
     return rec
 
 
-def cpu_baseline(st, budget_s: float, max_passes: int = 3):
-    """Time the CPU oracle (all host threads) on a bounded sample of the same
-    workload: whole params in order until about budget_s of oracle time (the
-    whole layer when it fits, then up to max_passes passes over the same
-    params, best pass reported).  The GPU's shards of those params are
-    compared bit for bit on the first pass."""
+def cpu_baseline(st, budget_s: float) -> dict:
+    """Time the CPU oracle (all host threads) on the same workload: params
+    in order, each read back in blocks of consecutive flat indices through
+    pinned buffers (all R ranks' gradients of the block and the GPU's result
+    words), each block reduced by the oracle as a 1-D problem of its own and
+    compared bit for bit with the GPU.  Whole params are taken until about
+    budget_s of oracle time (the whole layer when it fits).  The oracle's
+    rate is the algorithmic bytes over its compute time; the copy time is
+    reported beside it, not counted.  One thread is timed on one block."""
     import numpy as np
-    import torch
 
     import oracle
+    from shard_placement_amd import harness
 
     w = st.w
-    _, m, off, _ = oracle.layout(w.shapes, w.R)
-    used, kept, nbytes, t_total, t_d2h, mism = [], [], 0, 0.0, 0.0, 0
+    R = w.R
+    _, m, off, _ = oracle.layout(w.shapes, R)
+    reader = harness.BlockReader(st, m, off)
+    used, nbytes, t_total, mism, first = [], 0, 0.0, 0, None
+    t_wall = time.perf_counter()
     for p, shp in enumerate(w.shapes):
-        n = 1
-        for d in shp:
-            n *= d
-        t0 = time.perf_counter()
-        g = [[st.grads[q][p].reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)]
-             for q in range(w.R)]
-        got = [st.out[r][int(off[p]):int(off[p]) + int(m[p])].view(torch.int32).cpu().numpy()
-               for r in range(w.R)]
-        t_d2h += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        want = oracle.rs([shp], w.R, g)
-        t_total += time.perf_counter() - t0
-        for r in range(w.R):
-            mism += int(np.count_nonzero(got[r].view(np.uint32) != want[r][:int(m[p])].view(np.uint32)))
+        for a, b, g, got in reader.blocks(p):
+            L = b - a
+            t0 = time.perf_counter()
+            arenas = oracle.rs([(L,)], R, [[gq] for gq in g])
+            t_total += time.perf_counter() - t0
+            s = -(-L // R)
+            want = np.concatenate([x[:s] for x in arenas])[:L].view(np.uint32)
+            mism += int(np.count_nonzero(got != want))
+            nbytes += R * L * 2 + L * 4
+            if first is None:
+                first = [gq.copy() for gq in g]
         used.append(p)
-        nbytes += w.R * n * 2 + n * 4
-        kept.append((shp, g))
         if t_total >= budget_s:
             break
-    passes = [t_total]
-    # repeat the same sample (host copies kept) while the budget allows
-    while len(passes) < max_passes and sum(passes) + passes[0] <= budget_s:
-        t0 = time.perf_counter()
-        for shp, g in kept:
-            oracle.rs([shp], w.R, g)
-        passes.append(time.perf_counter() - t0)
-    best = min(passes)
+    t_wall = time.perf_counter() - t_wall
     cores = oracle.max_threads()
-    # one thread on the same sample, when that fits the budget (else on the
-    # first param of it)
-    one_sample = kept if best * cores <= budget_s else kept[:1]
-    one_bytes = sum(w.R * int(np.prod(shp)) * 2 + int(np.prod(shp)) * 4 if len(shp) else w.R * 2 + 4
-                    for shp, _ in one_sample)
+    # one thread on the first block, repeated for about a second
+    L1 = first[0].size
     oracle.set_threads(1)
     try:
-        t0 = time.perf_counter()
-        for shp, g in one_sample:
-            oracle.rs([shp], w.R, g)
-        t_one = time.perf_counter() - t0
+        reps, t_one = 0, 0.0
+        while reps < 1 or (t_one < 1.0 and reps < 50):
+            t0 = time.perf_counter()
+            oracle.rs([(L1,)], R, [[gq] for gq in first])
+            t_one += time.perf_counter() - t0
+            reps += 1
     finally:
         oracle.set_threads(cores)
+    whole = len(used) == w.P
     return {
-        "value": round(nbytes / best / 1e9, 3), "unit": "GB/s",
+        "value": round(nbytes / t_total / 1e9, 3), "unit": "GB/s",
         "cores": cores, "kind": "oracle",
-        "one_thread": {"value": round(one_bytes / t_one / 1e9, 3), "unit": "GB/s",
-                       "sample": "%d of the sample's params, one pass" % len(one_sample)},
-        "sample": "reduce-scatter of params %s of %s (R=%d, %.2f GB algorithmic; best of %d "
-                  "passes, %.2f s; device->host copy %.1f s not counted); GPU shards of these "
-                  "params bit-exact: %s" % (
-                      ",".join(w.names[p] for p in used), w.name, w.R, nbytes / 1e9,
-                      len(passes), best, t_d2h,
+        "one_thread": {"value": round(reps * (R * L1 * 2 + L1 * 4) / t_one / 1e9, 3),
+                       "unit": "GB/s",
+                       "sample": "one block of %d elements per rank, %d passes" % (L1, reps)},
+        "sample": "reduce-scatter of %s of %s (R=%d, %.2f GB algorithmic), read back in blocks "
+                  "of %d flat indices per rank, each reduced by the oracle (one pass, %.2f s of "
+                  "oracle time; %.1f s waiting for device->host copies, %.1f s wall, not "
+                  "counted); GPU shards of these params bit-exact: %s" % (
+                      "every param" if whole else "params " + ",".join(w.names[p] for p in used),
+                      w.name, R, nbytes / 1e9, reader.block, t_total, reader.copy_s, t_wall,
                       "yes" if mism == 0 else "NO (%d words differ)" % mism),
+        "params_checked": len(used),
+        "elements_checked": nbytes // (2 * R + 4),
         "parity_mismatches": mism,
     }
+
+
+def others_leg(keys, args, reps: int = 10) -> dict:
+    """RS and AG rates of other workloads in the default launch
+    configuration (event time on the launch stream, after two warm-up
+    steps), one workload allocated at a time."""
+    import torch
+
+    from shard_placement_amd import configs, harness
+
+    out = {}
+    for k in keys:
+        w = configs.get(k)
+        st = harness.setup(w, guard=0, flags=args.flags, rank_layout=args.rank_layout)
+        for _ in range(2):
+            st.plan.ag()
+            st.plan.rs()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for _ in range(reps):
+            st.plan.rs()
+        ev[1].record()
+        for _ in range(reps):
+            st.plan.ag()
+        ev[2].record()
+        torch.cuda.synchronize()
+        rs_ms = ev[0].elapsed_time(ev[1]) / reps
+        ag_ms = ev[1].elapsed_time(ev[2]) / reps
+        rsb, agb = harness.rs_bytes(w), harness.ag_bytes(w)
+        info = st.plan.info
+        out[w.name] = {
+            "R": w.R, "P": w.P, "N": w.numel(), "slot_reuse": w.slot_reuse,
+            "rs_ms": round(rs_ms, 4), "rs_gbps": round(rsb / (rs_ms * 1e-3) / 1e9, 1),
+            "rs_frac_hbm": round(rsb / (rs_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "rs_launches": -(-int(info.rs_tiles) // max(1, int(info.rs_launch_tiles))),
+            "ag_ms": round(ag_ms, 4), "ag_gbps": round(agb / (ag_ms * 1e-3) / 1e9, 1),
+            "ag_frac_hbm": round(agb / (ag_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("other workload", w.name, out[w.name])
+        st.free()
+        del st
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -381,7 +446,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="2", help="workload key or name (default: the Llama-3.1-70B layer, R=8)")
+    ap.add_argument("--workload", default="5",
+                    help="workload key or name (default: the Llama-3.1-70B layer plus a ragged "
+                         "param at R=64 with Slot-Reuse)")
     ap.add_argument("--flags", type=int, default=-1, help="TIDE_FLAG_* access hints (-1: default)")
     ap.add_argument("--rs-tile", type=int, default=0)
     ap.add_argument("--launch-mib", type=int, default=0, help="MiB per kernel launch (0: default, -1: one launch)")
@@ -403,6 +470,8 @@ def main():
                     help="skip the two-phase pipeline emulation leg")
     ap.add_argument("--no-stock", action="store_true",
                     help="skip timing the stock-FSDP2 analog (pack, add, copy out in torch ops)")
+    ap.add_argument("--others", default="2,3,4",
+                    help="other workload keys timed after the main one (RS and AG only); '' for none")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of a plain device copy run once (counter calibration)")
     args = ap.parse_args()
@@ -590,6 +659,7 @@ def main():
         probe = probe_mod.run(modes, rsb, iters=40)
         for m in probe["modes"]:
             log("probe", m)
+        del modes
 
     traffic_ratio = read_traffic("rs_fixed_kernel", w.name, RS_SOURCES)
     cpu = None
@@ -659,6 +729,22 @@ def main():
         "env": {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
                 "hip": torch.version.hip, "host_threads": len(os.sched_getaffinity(0))},
     }
+    # the pages' figures (other hardware) beside this GPU's analogs of them
+    ctx = dict(PAGES_CONTEXT)
+    ctx["one_gpu_analogs"] = {
+        "gemm_slowdown_pct": rec["gemm_slowdown_pct"],
+        "stock_analog_pack_pct_of_its_rs": (round(100 * stock_rec["pack_ms"] / stock_rec["rs_ms"], 1)
+                                            if stock_rec else None),
+        "fused_rs_speedup_over_stock_analog": stock_rec["fused_rs_speedup"] if stock_rec else None,
+    }
+    rec["pages_context"] = ctx
+    keys = [k for k in args.others.split(",") if k.strip() and configs.get(k).key != w.key]
+    if keys:
+        st.free()
+        del st
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rec["others"] = others_leg(keys, args)
     print(json.dumps(rec), flush=True)
     if cpu and cpu.get("parity_mismatches"):
         sys.exit(3)

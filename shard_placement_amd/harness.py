@@ -160,3 +160,74 @@ def stage_buffers(st: Setup, slot_stride: int = 0, rank_layout: str = "packed",
         rows[r].view(torch.int16).fill_(BF16_SENTINEL)
         out.append(rows[r][offset:offset + n])
     return out
+
+
+class BlockReader:
+    """Reads one workload's reduce-scatter inputs and results back to the
+    host in blocks of consecutive flat indices of one parameter, through
+    pinned buffers, so that a whole layer can be checked on the CPU with
+    bounded host memory.
+
+    The caller supplies the shard geometry (chunk numel m[p] and arena
+    offset off[p] of every param) that says where the results of a flat
+    index lie: rank j // m[p], element off[p] + j % m[p] of its arena.
+    Two buffer sets alternate: the copies of block k + 1 run while the
+    caller works on block k.  Each block holds the R ranks' bf16 bits
+    (uint16) and the result words (uint32) for flat indices [a, b); the
+    arrays handed out stay valid until the next block is requested."""
+
+    def __init__(self, st: Setup, m, off, block_bytes: int = 512 << 20):
+        self.st = st
+        self.m = [int(x) for x in m]
+        self.off = [int(x) for x in off]
+        R = st.w.R
+        self.block = max(1 << 16, block_bytes // (2 * R) // 4096 * 4096)
+        self.g = [torch.empty((R, self.block), dtype=torch.int16, pin_memory=True) for _ in range(2)]
+        self.o = [torch.empty(self.block, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.stream = torch.cuda.Stream(device=st.device)
+        self.copy_s = 0.0  # host time spent waiting for copies
+
+    def _issue(self, k: int, p: int, a: int, b: int):
+        st, R = self.st, self.st.w.R
+        mp, L = self.m[p], b - a
+        ev = torch.cuda.Event()
+        self.stream.wait_stream(torch.cuda.current_stream(st.device))
+        with torch.cuda.stream(self.stream):
+            for q in range(R):
+                src = st.grads[q][p].reshape(-1)[a:b].view(torch.int16)
+                self.g[k][q, :L].copy_(src, non_blocking=True)
+            pos = 0
+            for r in range(a // mp, (b - 1) // mp + 1):
+                lo, hi = max(a, r * mp), min(b, (r + 1) * mp)
+                base = self.off[p] - r * mp
+                src = st.out[r][base + lo: base + hi].view(torch.int32)
+                self.o[k][pos:pos + hi - lo].copy_(src, non_blocking=True)
+                pos += hi - lo
+            ev.record(self.stream)
+        return ev
+
+    def blocks(self, p: int):
+        """Yield (a, b, grads, out): grads a list of R uint16 arrays of b - a
+        elements, out a uint32 array of b - a result words."""
+        import time
+
+        import numpy as np
+
+        shp = self.st.w.shapes[p]
+        n = 1
+        for d in shp:
+            n *= int(d)
+        if n == 0 or self.m[p] == 0:
+            return
+        spans = [(a, min(n, a + self.block)) for a in range(0, n, self.block)]
+        pending = self._issue(0, p, *spans[0])
+        for i, (a, b) in enumerate(spans):
+            k = i & 1
+            t0 = time.perf_counter()
+            pending.synchronize()
+            self.copy_s += time.perf_counter() - t0
+            if i + 1 < len(spans):
+                pending = self._issue(k ^ 1, p, *spans[i + 1])
+            L = b - a
+            g = [self.g[k][q, :L].numpy().view(np.uint16) for q in range(self.st.w.R)]
+            yield a, b, g, self.o[k][:L].numpy().view(np.uint32)

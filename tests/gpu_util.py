@@ -92,22 +92,6 @@ def check_out_guards(st, r):
             "rank %d: guard band written" % r
 
 
-def check_rs_by_param(st, params, order="fixed"):
-    """Bit-exact oracle comparison of whole params (read back one param at a
-    time, so host memory stays bounded)."""
-    w = st.w
-    _, m, off, _ = oracle.layout(w.shapes, w.R, _align_of(st))
-    for p in params:
-        shp = w.shapes[p]
-        say("oracle full param", w.name, p, shp)
-        g = grads_np(st, p)
-        want = oracle.rs([shp], w.R, g, order=order)
-        for r in range(w.R):
-            got = bits32(st.out[r][int(off[p]):int(off[p]) + int(m[p])])
-            assert_bits_equal(got, want[r][:int(m[p])].view(np.uint32),
-                              "%s param %d rank %d" % (w.name, p, r))
-
-
 def check_rs_sampled(st, order="fixed", per_shard=64, edge=16, seed=0):
     """Bit-exact oracle comparison on sampled elements of every (param, rank)
     shard: its first and last `edge` elements plus `per_shard` random ones.
@@ -220,3 +204,41 @@ def check_ag_full(st):
     if guard:
         fa = bits16(st.full_arena)
         assert np.all(fa[:guard] == SENT16) and np.all(fa[-guard:] == SENT16), "AG guard band written"
+
+
+def check_rs_whole(st, order="fixed", block_bytes=512 << 20):
+    """Every element of every shard of the layer against the oracle, bit for
+    bit, with bounded host memory: each param is read back in blocks of
+    consecutive flat indices (all R ranks' values of those indices and the
+    result words the arenas hold for them), and the oracle reduces each
+    block as a 1-D problem of its own (the sum of an element does not
+    depend on where the shard boundaries fall, so the concatenated shards of
+    that sub-problem are the block's expected results).  Padding words are
+    checked for +0.0 on the device.  Returns the number of elements."""
+    from shard_placement_amd import harness
+
+    w = st.w
+    R = w.R
+    _, m, off, _ = oracle.layout(w.shapes, R, _align_of(st))
+    reader = harness.BlockReader(st, m, off, block_bytes)
+    total = 0
+    for p, shp in enumerate(w.shapes):
+        n, mp = numel(shp), int(m[p])
+        say("whole-layer oracle check", w.name, "param", p, shp, order)
+        for a, b, g, got in reader.blocks(p):
+            L = b - a
+            arenas = oracle.rs([(L,)], R, [[gq] for gq in g], order=order)
+            s = -(-L // R)
+            want = np.concatenate([x[:s] for x in arenas])[:L]
+            assert_bits_equal(got, want.view(np.uint32),
+                              "%s param %d flat [%d, %d)" % (w.name, p, a, b))
+            total += L
+        for r in range(R):
+            lo = max(0, n - r * mp)
+            if lo < mp:
+                pad = st.out[r][int(off[p]) + lo:int(off[p]) + mp]
+                assert bool(torch.all(pad.view(torch.int32) == 0)), \
+                    "%s param %d rank %d: padding not +0.0" % (w.name, p, r)
+    say("whole-layer oracle check done", w.name, total, "elements; copies waited %.1f s"
+        % reader.copy_s)
+    return total
