@@ -254,7 +254,12 @@ tide_status tide_ag_place_sdma_streams(const void *h_plan, const tide_stream_t *
  * bytes so far) [Abstract: transport and placement kept off the compute
  * units].
  * Host-synchronous: waits for `stream` to finish its earlier work, then
- * returns when every copy has completed (no kernel runs).  Do not overlap
+ * returns when every copy has completed (no kernel runs).  Both waits are
+ * bounded: at most 60 s for the stream, and 10 s plus 1 s per GB of copies
+ * for the engines; past either deadline the call returns TIDE_EHIP.  After a
+ * timeout on the copies they may still be running and writing their
+ * destinations, so the caller must not free or reuse those buffers before
+ * the device has been synchronised.  Do not overlap
  * it with the runtime's own copy-engine copies (tide_ag_place_sdma, D2H
  * copies) on the same device.  TIDE_EUNSUPPORTED: the device has no copy
  * engine the runtime reports. */
@@ -280,7 +285,7 @@ tide_status tide_dma_engine_count(int32_t *count);
  * rank q, the valid part of rank q's slice of p (flat indices [r*m_p,
  * r*m_p + v*c), v = clamp(d0 - r*s, 0, s)) is copied by the DMA engines to
  * slot q of h_stage[r] at element off[p]; padding rows are not copied.
- * Host-synchronous like tide_ag_place_dma.
+ * Host-synchronous, with the same bounded waits, as tide_ag_place_dma.
  *
  * Phase 2, tide_rs_fold_staged: a kernel folds each rank's R slots into its
  * fp32 arena with the reduce-scatter's tiles, rank order and bits (padding

@@ -24,11 +24,14 @@
 #include <hsa/hsa_ext_amd.h>
 
 #include <algorithm>
+#include <chrono>
 #include <climits>
 #include <cstring>
 #include <mutex>
+#include <thread>
 #include <vector>
 
+#include "bounded_wait.h"
 #include "plan_format.h"
 #include "stage_check.h"
 #include "tide.h"
@@ -137,9 +140,38 @@ struct Copy {
     size_t bytes;
 };
 
-// Issue the copies over all engines and wait for them.
+// Wait for the caller's stream to finish its earlier work, polling with
+// short sleeps, for at most kStreamTimeoutNs.
+tide_status drain_stream(tide_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t last = hipSuccess;
+    const bool done = wait_until(
+        [&] {
+            last = hipStreamQuery(s);
+            return last != hipErrorNotReady;
+        },
+        [](uint64_t ns) {
+            std::this_thread::sleep_for(std::chrono::nanoseconds(ns < 20000 ? ns : 20000));
+        },
+        kStreamTimeoutNs);
+    return done && last == hipSuccess ? TIDE_OK : TIDE_EHIP;
+}
+
+// ROCr's wait takes its timeout hint in system timestamp ticks.
+uint64_t ns_to_ticks(uint64_t ns) {
+    static const uint64_t hz = [] {
+        uint64_t f = 0;
+        if (hsa_system_get_info(HSA_SYSTEM_INFO_TIMESTAMP_FREQUENCY, &f) != HSA_STATUS_SUCCESS || !f)
+            f = 1000000000ull;
+        return f;
+    }();
+    return (uint64_t)((double)ns * (double)hz * 1e-9) + 1;
+}
+
+// Issue the copies over all engines and wait for them (bounded: a call whose
+// copies stop making progress returns TIDE_EHIP after copy_timeout_ns).
 tide_status run_copies(std::vector<Copy>& copies, tide_stream_t stream) {
-    if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return TIDE_EHIP;
+    if (drain_stream(stream) != TIDE_OK) return TIDE_EHIP;
     copies.erase(std::remove_if(copies.begin(), copies.end(), [](const Copy& c) { return c.bytes == 0; }),
                  copies.end());
     if (copies.empty()) return TIDE_OK;
@@ -167,8 +199,20 @@ tide_status run_copies(std::vector<Copy>& copies, tide_stream_t stream) {
     }
     if (issued < copies.size())  // the copies never issued will not decrement the signal
         hsa_signal_subtract_screlease(sig, (hsa_signal_value_t)(copies.size() - issued));
-    while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX,
-                                     HSA_WAIT_STATE_BLOCKED) != 0) {
+    uint64_t total = 0;
+    for (const Copy& c : copies) total += c.bytes;
+    const bool done = wait_until(
+        [&] { return hsa_signal_load_scacquire(sig) == 0; },
+        [&](uint64_t ns) {
+            (void)hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_EQ, 0, ns_to_ticks(ns),
+                                            HSA_WAIT_STATE_BLOCKED);
+        },
+        copy_timeout_ns(total));
+    if (!done) {
+        // Copies may still be in flight and will decrement the signal when
+        // they end: it is left alive (a small leak) rather than destroyed
+        // under them.
+        return TIDE_EHIP;
     }
     hsa_signal_destroy(sig);
     return st;
