@@ -269,13 +269,12 @@ void cut_ag_run(std::vector<AgTile>& out, int32_t p, int64_t src, int64_t dst, i
     if (len <= 0) return;
     uint64_t sa = gaddr + 2 * (uint64_t)src, da = faddr + 2 * (uint64_t)dst;
     if (sa % 16 != da % 16) {
-        // Realigning copy: destination 16-byte aligned from `head` on, with at
-        // least 8 elements before and after the body inside this run, so the
-        // 16-byte-aligned source loads around the body stay within the run.
-        int64_t head = (int64_t)(((16 - da % 16) % 16) / 2);
-        if (head < 8) head += 8;
-        const int64_t body = len - head - 8 > 0 ? ((len - head - 8) / kVec) * kVec : 0;
-        if (body >= (int64_t)kBlock * kVec) {
+        // Realigning copy: destination 16-byte aligned from `head` on; the
+        // kernel reads the (2-byte-aligned) source 16 bytes at a time from
+        // exactly the tile's own elements.
+        const int64_t head = std::min<int64_t>(len, (int64_t)(((16 - da % 16) % 16) / 2));
+        const int64_t body = ((len - head) / kVec) * kVec;
+        if (body > 0) {
             emit(src, dst, head, kAgScalar);
             emit(src + head, dst + head, body, kAgShift);
             emit(src + head + body, dst + head + body, len - head - body, kAgScalar);

@@ -89,9 +89,8 @@ enum AgKind : int32_t {
     kAgVec16 = 0,   // both ends 16-byte aligned, len % 8 == 0
     kAgVec4 = 1,    // both ends 4-byte aligned, len % 2 == 0
     kAgScalar = 2,  // 2-byte elements
-    kAgShift = 3,   // destination 16-byte aligned, source not; len % 8 == 0 and
-                    // at least 8 elements of the same run before and after the
-                    // tile (the realigning loads read up to 16 bytes around it)
+    kAgShift = 3,   // destination 16-byte aligned, source not (16-byte loads
+                    // from a 2-byte-aligned address); len % 8 == 0
 };
 
 struct AgTile {
