@@ -379,6 +379,28 @@ tide_status tide_pipeline_run(tide_pipeline_t pipeline, const void *h_plan, cons
                               int32_t phase2, tide_stream_t stream);
 tide_status tide_pipeline_destroy(tide_pipeline_t pipeline);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the two
+ * phases above over tiles [tile_begin, tile_begin + tile_count) --
+ * tide_rs_tiles_to_stage into a staging chunk, then tide_rs_stage_to_shards
+ * from it into the shard arenas, both on `stream` -- with the staging chunk
+ * in the library's own device array of TIDE_SCRATCH_BYTES instead of caller
+ * memory.  The array is part of the library's code object: each device the
+ * library runs on holds one until the process ends.  The results are those
+ * of the two calls (and of tide_rs_bf16_to_fp32 with order 0 for the same
+ * tiles).  tile_count * rs_tile_elems * 4 must not exceed
+ * TIDE_SCRATCH_BYTES (TIDE_ENOSPACE otherwise; 4096 tiles of the default
+ * 2048 elements fit); other checks as for tide_rs_tiles_to_stage.  Nothing
+ * in the array needs clearing between calls (phase 1 writes every word that
+ * phase 2 reads).  Calls and the library allocate nothing.  All calls on one
+ * device share its array: calls issued one after another on one stream are
+ * ordered, calls that overlap in time on one device (other streams or host
+ * threads) race and give undefined results. */
+#define TIDE_SCRATCH_BYTES (32u << 20)
+tide_status tide_rs_two_phase_noalloc(const void *h_plan, const void *d_plan,
+                                      int64_t tile_begin, int64_t tile_count,
+                                      int32_t max_workgroups, tide_stream_t stream);
+
 /* Static text for a status code. */
 const char *tide_status_str(int32_t status);
 

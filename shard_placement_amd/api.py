@@ -218,6 +218,17 @@ def tide_rs_stage_to_shards_sdma(h_plan: np.ndarray, tile_begin: int, tile_count
           "tide_rs_stage_to_shards_sdma")
 
 
+def tide_rs_two_phase_noalloc(h_plan: np.ndarray, d_plan: torch.Tensor, tile_begin: int,
+                              tile_count: int, max_workgroups: int = 0, stream=None) -> None:
+    """Both pipeline phases over tiles [tile_begin, +tile_count) through the
+    library's own staging array (no allocation by anyone; at most
+    TIDE_SCRATCH_BYTES of staging per call)."""
+    check(_lib.lib().tide_rs_two_phase_noalloc(h_plan.ctypes.data, d_plan.data_ptr(),
+                                               int(tile_begin), int(tile_count),
+                                               int(max_workgroups), _stream(stream)),
+          "tide_rs_two_phase_noalloc")
+
+
 def tide_stream_create_cu_limited(n_cu: int) -> torch.cuda.ExternalStream:
     """A torch stream wrapping a HIP stream confined to the first n_cu CUs.
     Release it with tide_stream_destroy."""

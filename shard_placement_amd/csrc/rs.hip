@@ -27,6 +27,7 @@
 
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 #include "plan_format.h"
 #include "stage_check.h"
@@ -849,4 +850,62 @@ extern "C" tide_status tide_rs_bf16_to_fp32_census(const void* h_plan, const voi
                                                    tide_stream_t stream) {
     if (!census) return TIDE_EINVAL;
     return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream, census, census_len);
+}
+
+// ---- the two phases through the library's own staging array
+//
+// For callers that cannot allocate device memory: the staging chunk of the
+// two-phase calls is a file-scope device array instead of caller memory.
+// In host code `scratch` names a host-side stand-in, not the device array:
+// its device address is looked up once per device (with that device
+// current) and only that address is ever handed to kernels.
+namespace {
+
+static_assert(TIDE_SCRATCH_BYTES % 256 == 0, "the staging array is whole 256-byte blocks");
+static __device__ __align__(256) float scratch[TIDE_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kScratchDevices];  // device address of `scratch`, per device
+
+tide_status scratch_of_current_device(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TIDE_EHIP;
+    if (dev < 0 || dev >= kScratchDevices) return TIDE_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TIDE_EHIP;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch[dev];
+    return TIDE_OK;
+}
+
+}  // namespace
+
+extern "C" tide_status tide_rs_two_phase_noalloc(const void* h_plan, const void* d_plan,
+                                                 int64_t tile_begin, int64_t tile_count,
+                                                 int32_t max_workgroups, tide_stream_t stream) {
+    // every host-side check before the first HIP call
+    if (!h_plan || !d_plan) return TIDE_EINVAL;
+    PlanHeader h;
+    std::memcpy(&h, h_plan, sizeof h);
+    if (h.magic != kMagic || h.version != kVersion) return TIDE_EPLAN;
+    if (!h.has_rs) return TIDE_EUNSUPPORTED;
+    if (max_workgroups < 0 || tile_begin < 0 || tile_count < 0 || tile_begin > h.n_rs_tiles ||
+        tile_count > h.n_rs_tiles - tile_begin)
+        return TIDE_EINVAL;
+    const int64_t cap = (int64_t)(TIDE_SCRATCH_BYTES / sizeof(float));
+    if (h.rs_tile <= 0 || tile_count > cap / h.rs_tile) return TIDE_ENOSPACE;
+    if (reinterpret_cast<uintptr_t>(d_plan) % 16) return TIDE_EALIGN;
+    if (tile_count == 0) return TIDE_OK;
+    float* stage = nullptr;
+    tide_status st = scratch_of_current_device(&stage);
+    if (st != TIDE_OK) return st;
+    st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, cap, max_workgroups, &h);
+    if (st != TIDE_OK) return st;
+    st = issue_tiles_to_stage(h, d_plan, tile_begin, tile_count, stage, max_workgroups, stream);
+    if (st != TIDE_OK) return st;
+    return issue_stage_to_shards(h, d_plan, tile_begin, tile_count, stage, max_workgroups, stream);
 }

@@ -561,3 +561,35 @@ def test_product_path_never_touches_the_oracle():
             mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
             assert all(not m.startswith("shard_placement_amd") for m in mods)
 
+
+def test_noalloc_two_phase_validates_before_touching_the_gpu():
+    """The allocation-free two-phase call checks its plan, tile range and
+    the size of its staging array on the host, before any HIP call; an
+    empty range is a no-op."""
+    L = _lib.lib()
+    with open(os.path.join(ROOT, "include", "tide.h")) as fh:
+        m = re.search(r"#define TIDE_SCRATCH_BYTES \((\d+)u << (\d+)\)", fh.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.SCRATCH_BYTES
+    shapes = [(8192, 4096), (5,)]
+    R = 2
+    _, _, _, S = api.tide_desc_geometry(shapes, R)
+    g, o, ga, f = _fake_ptrs(shapes, R, S)
+    blob, info = api.tide_desc_build(shapes, R, g, o, None, None, rs_tile=2048)
+    n, T = int(info.rs_tiles), int(info.rs_tile_elems)
+    cap = _lib.SCRATCH_BYTES // (4 * T)
+    assert n > cap
+    fake_dev = ctypes.c_void_p(1 << 44)
+    F = L.tide_rs_two_phase_noalloc
+
+    def call(b=0, cnt=1, mw=0, plan=blob, dev=fake_dev):
+        return F(plan.ctypes.data if plan is not None else None, dev, b, cnt, mw, None)
+    assert call(plan=None) == -1 and call(dev=None) == -1
+    assert call(plan=np.zeros(4096, np.uint8)) == -7
+    ag_blob, _ = api.tide_desc_build(shapes, R, None, None, ga, f)
+    assert call(plan=ag_blob) == -6
+    assert call(b=-1) == -1 and call(cnt=-1) == -1 and call(mw=-1) == -1
+    assert call(b=n, cnt=1) == -1 and call(b=n - 1, cnt=2) == -1
+    assert call(cnt=cap + 1) == -4                      # more than the array holds
+    assert call(b=n - cap - 1, cnt=cap + 1) == -4
+    assert call(dev=ctypes.c_void_p((1 << 44) + 8)) == -2
+    assert call(cnt=0) == 0 and call(b=n, cnt=0) == 0   # nothing to do
