@@ -470,6 +470,8 @@ def main():
                     help="skip the two-phase pipeline emulation leg")
     ap.add_argument("--no-stock", action="store_true",
                     help="skip timing the stock-FSDP2 analog (pack, add, copy out in torch ops)")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="skip the traced call (CU census and per-tile timing)")
     ap.add_argument("--others", default="2,3,4",
                     help="other workload keys timed after the main one (RS and AG only); '' for none")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
@@ -483,7 +485,7 @@ def main():
 
     import torch
 
-    from shard_placement_amd import configs, harness
+    from shard_placement_amd import configs, harness, profiling
 
     if not torch.cuda.is_available():
         print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
@@ -601,18 +603,29 @@ def main():
                 "engine": "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run"}
         log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
 
-    # which compute units the reduce-scatter ran on (one census call, outside
-    # the timed region: same launches, each tile records its CU's hardware id)
-    census = st.plan.rs_census(max_workgroups=args.max_wg)
-    torch.cuda.synchronize()
-    ids = census.cpu().tolist()
-    cus_measured = len(set(ids))
-    per_xcc = {}
-    for v in set(ids):
-        per_xcc[v >> 8] = per_xcc.get(v >> 8, 0) + 1
-    log("census: %d distinct CUs over %d tiles; per XCC %s" % (cus_measured, len(ids),
-                                                              dict(sorted(per_xcc.items()))))
-    del census
+    # which compute units the reduce-scatter ran on, and for how long (one
+    # traced call outside the timed region: same launches, each tile records
+    # its CU's hardware id and its start and end on the real-time counter)
+    cu_rec, cus_measured, per_xcc = {"held_cu_ms": None}, None, {}
+    if not args.no_trace:
+        st.plan.rs_trace(max_workgroups=args.max_wg)
+        torch.cuda.synchronize()
+        te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        te0.record()
+        census, stamps = st.plan.rs_trace(max_workgroups=args.max_wg)
+        te1.record()
+        torch.cuda.synchronize()
+        ids = census.cpu().numpy()
+        cu_rec = profiling.cu_time(ids, stamps.cpu().numpy())
+        cu_rec["traced_call_ms_events"] = round(te0.elapsed_time(te1), 4)
+        cus_measured = cu_rec["cus"]
+        for v in set(ids.tolist()):
+            per_xcc[v >> 8] = per_xcc.get(v >> 8, 0) + 1
+        log("census: %d distinct CUs over %d tiles; per XCC %s; CU time %s" % (
+            cus_measured, len(ids), dict(sorted(per_xcc.items())), cu_rec))
+        st.plan.rs()  # the untraced result for the checks below
+        torch.cuda.synchronize()
+        del census, stamps
 
     dma_rec = staged_rec = None
     if not args.no_staged:
@@ -707,7 +720,11 @@ def main():
         "rs_lds_per_workgroup": int(info.rs_lds_bytes),
         "rs_cus": cus_measured,
         "rs_cus_per_xcc": {str(k): v for k, v in sorted(per_xcc.items())},
-        "rs_cu_ms": round(cus_measured * rs_avg, 1),
+        # CU time the reduce-scatter held (per CU, the union of its tiles'
+        # busy intervals, from the traced call), the one-GPU analog of the
+        # pages' reduce-scatter "SM time"
+        "rs_cu_ms": cu_rec["held_cu_ms"],
+        "rs_cu_time": cu_rec if not args.no_trace else None,
         "ag_dma": dma_rec,
         "staged_rs": staged_rec,
         "pipeline": pipe_rec,
@@ -731,8 +748,15 @@ def main():
     }
     # the pages' figures (other hardware) beside this GPU's analogs of them
     ctx = dict(PAGES_CONTEXT)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     ctx["one_gpu_analogs"] = {
         "gemm_slowdown_pct": rec["gemm_slowdown_pct"],
+        "rs_cu_ms_fused": cu_rec["held_cu_ms"],
+        # the analog's torch kernels have grids of far more than one
+        # workgroup per CU: all CUs for its whole duration
+        "rs_cu_ms_stock_analog": round(n_cu * stock_rec["rs_ms"], 1) if stock_rec else None,
+        "rs_cu_time_stock_over_fused": (round(n_cu * stock_rec["rs_ms"] / cu_rec["held_cu_ms"], 2)
+                                        if stock_rec and cu_rec.get("held_cu_ms") else None),
         "stock_analog_pack_pct_of_its_rs": (round(100 * stock_rec["pack_ms"] / stock_rec["rs_ms"], 1)
                                             if stock_rec else None),
         "fused_rs_speedup_over_stock_analog": stock_rec["fused_rs_speedup"] if stock_rec else None,

@@ -220,6 +220,21 @@ tide_status tide_rs_bf16_to_fp32_census(const void *h_plan, const void *d_plan,
                                         uint32_t *census, int64_t census_len,
                                         tide_stream_t stream);
 
+/* The census call that also times every tile: census[t] as above, and
+ * stamps[2t], stamps[2t + 1] the GPU's constant-rate real-time counter
+ * (100 MHz on MI355X: 10 ns ticks) read when the tile's workgroup starts it
+ * and after all of the workgroup's waves have finished it.  From them the
+ * caller gets the compute-unit time the reduce-scatter actually held (per
+ * CU, the union of the intervals of its tiles), the occupancy-weighted
+ * analog of the pages' reduce-scatter "SM time" [Abstract; Performance].
+ * census: >= len uint32 words, stamps: >= 2 * len uint64 words (device
+ * memory, 4- and 8-byte aligned), len >= rs_tiles.  The timing adds one
+ * workgroup barrier per tile; results are those of tide_rs_bf16_to_fp32. */
+tide_status tide_rs_bf16_to_fp32_trace(const void *h_plan, const void *d_plan,
+                                       int32_t order, int32_t max_workgroups,
+                                       uint32_t *census, uint64_t *stamps, int64_t len,
+                                       tide_stream_t stream);
+
 /* All-gather placement on the compute units [Abstract: TIDE-AG]: for
  * every param p and rank r, the clamp(d0 - r*s, 0, s) valid rows of slot r
  * are copied to rows [r*s, ...) of full[p]; slot padding is never read.

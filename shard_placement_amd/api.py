@@ -138,6 +138,22 @@ def tide_rs_bf16_to_fp32_census(h_plan: np.ndarray, d_plan: torch.Tensor, census
           "tide_rs_bf16_to_fp32_census")
 
 
+def tide_rs_bf16_to_fp32_trace(h_plan: np.ndarray, d_plan: torch.Tensor, census: torch.Tensor,
+                               stamps: torch.Tensor, order: int = 0, max_workgroups: int = 0,
+                               stream=None) -> None:
+    """The census call that also records each tile's start and end on the
+    GPU's real-time counter (stamps: int64, two per tile)."""
+    if census.dtype != torch.int32 or census.device.type != "cuda" or not census.is_contiguous():
+        raise TideError(-6, "census must be a contiguous int32 GPU tensor")
+    if stamps.dtype != torch.int64 or stamps.device.type != "cuda" or not stamps.is_contiguous():
+        raise TideError(-6, "stamps must be a contiguous int64 GPU tensor")
+    n = min(census.numel(), stamps.numel() // 2)
+    check(_lib.lib().tide_rs_bf16_to_fp32_trace(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
+                                                int(max_workgroups), census.data_ptr(),
+                                                stamps.data_ptr(), n, _stream(stream)),
+          "tide_rs_bf16_to_fp32_trace")
+
+
 def tide_ag_place(h_plan: np.ndarray, d_plan: torch.Tensor, max_workgroups: int = 0,
                   stream=None) -> None:
     check(_lib.lib().tide_ag_place(h_plan.ctypes.data, d_plan.data_ptr(), int(max_workgroups),
@@ -384,6 +400,17 @@ class Plan:
         tide_rs_bf16_to_fp32_census(self.blob, self.d_blob, census, ORDERS[order],
                                     max_workgroups, stream)
         return census
+
+    def rs_trace(self, order: str = "fixed", max_workgroups: int = 0, stream=None):
+        """The reduce-scatter, returning (census, stamps): per tile the packed
+        compute-unit id (int32) and its start and end ticks on the GPU's
+        real-time counter (int64 [tiles, 2]); GPU tensors."""
+        n = max(1, int(self.info.rs_tiles))
+        census = torch.full((n,), -1, dtype=torch.int32, device=self.d_blob.device)
+        stamps = torch.zeros((n, 2), dtype=torch.int64, device=self.d_blob.device)
+        tide_rs_bf16_to_fp32_trace(self.blob, self.d_blob, census, stamps, ORDERS[order],
+                                   max_workgroups, stream)
+        return census, stamps
 
     def ag(self, max_workgroups: int = 0, stream=None) -> None:
         tide_ag_place(self.blob, self.d_blob, max_workgroups, stream)

@@ -100,6 +100,19 @@ __device__ __forceinline__ uint32_t hw_cu_id() {
     return ((xcc & 0xfu) << 8) | ((hw >> 8) & 0xffu);
 }
 
+// Optional per-tile timing: the GPU's constant-rate real-time counter read
+// when the workgroup starts the tile and after all its waves have finished
+// it, stored as stamps[2t], stamps[2t + 1].  The barrier only runs when
+// stamps is set (a uniform kernel argument).
+__device__ __forceinline__ void stamp_tile(uint64_t* stamps, int64_t t, uint64_t t_begin) {
+    if (!stamps) return;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        stamps[2 * t] = t_begin;
+        stamps[2 * t + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+}
+
 __device__ __forceinline__ const uint16_t* src_of(const uint64_t* gp, int q) {
     return reinterpret_cast<const uint16_t*>(gp[q]);
 }
@@ -382,12 +395,14 @@ __global__ __launch_bounds__(kBlock) void rs_tree_kernel(const RsTile* __restric
                                                          int64_t ntiles,
                                                          const uint64_t* __restrict__ gptr,
                                                          const uint64_t* __restrict__ obase,
-                                                         int R, uint32_t* __restrict__ census) {
+                                                         int R, uint32_t* __restrict__ census,
+                                                         uint64_t* __restrict__ stamps) {
     __shared__ float lds[kBlock * kVec];
     float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
     for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
         const int64_t t = tile_of(b, ntiles);
         if (census && threadIdx.x == 0) census[t] = hw_cu_id();
+        const uint64_t t_begin = stamps ? __builtin_amdgcn_s_memrealtime() : 0;
         const RsTile tile = tiles[t];
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
         const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
@@ -397,6 +412,7 @@ __global__ __launch_bounds__(kBlock) void rs_tree_kernel(const RsTile* __restric
             rs_scalar_tree<LEVELS>(src, R, tile.len, out);
         else
             rs_pad(tile.len, out);
+        stamp_tile(stamps, t, t_begin);
     }
 }
 
@@ -405,12 +421,14 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
                                                           int64_t ntiles,
                                                           const uint64_t* __restrict__ gptr,
                                                           const uint64_t* __restrict__ obase,
-                                                          int R, uint32_t* __restrict__ census) {
+                                                          int R, uint32_t* __restrict__ census,
+                                                          uint64_t* __restrict__ stamps) {
     __shared__ float lds[kBlock * kVec];
     float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
     for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
         const int64_t t = tile_of(b, ntiles);
         if (census && threadIdx.x == 0) census[t] = hw_cu_id();
+        const uint64_t t_begin = stamps ? __builtin_amdgcn_s_memrealtime() : 0;
         const RsTile tile = tiles[t];
         float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
         const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
@@ -420,6 +438,7 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
             rs_scalar_fixed(src, R, tile.len, out);
         else
             rs_pad(tile.len, out);
+        stamp_tile(stamps, t, t_begin);
     }
 }
 
@@ -535,7 +554,8 @@ __global__ __launch_bounds__(kBlock) void rs_drain_kernel(const RsTile* __restri
     }
 }
 
-typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int, uint32_t*);
+typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int, uint32_t*,
+                         uint64_t*);
 
 template <int RB, bool EXACT, int U>
 RsKernel pick_nt(uint32_t flags) {
@@ -661,7 +681,8 @@ unsigned rs_extra_lds(const PlanHeader& h) {
 
 tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int64_t tile_begin,
                       int64_t tile_count, int32_t max_workgroups, tide_stream_t stream,
-                      uint32_t* census = nullptr, int64_t census_len = 0) {
+                      uint32_t* census = nullptr, int64_t census_len = 0,
+                      uint64_t* stamps = nullptr) {
     if (!h_plan || !d_plan) return TIDE_EINVAL;
     PlanHeader h;
     std::memcpy(&h, h_plan, sizeof h);
@@ -675,7 +696,7 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         tile_count > h.n_rs_tiles - tile_begin)
         return TIDE_EINVAL;
     if (tile_count == 0) return TIDE_OK;
-    if (census && census_len < tile_count) return TIDE_EINVAL;
+    if ((census || stamps) && census_len < tile_count) return TIDE_EINVAL;
 
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
     const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
@@ -695,7 +716,8 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
         if (grid > INT_MAX) grid = INT_MAX;
         uint32_t* cen = census ? census + (b - tile_begin) : nullptr;
-        void* args[] = {&tiles, &ntiles, &gptr, &obase, &R, &cen};
+        uint64_t* stp = stamps ? stamps + 2 * (b - tile_begin) : nullptr;
+        void* args[] = {&tiles, &ntiles, &gptr, &obase, &R, &cen, &stp};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
                                        dim3(kBlock), args, rs_extra_lds(h),
                                        reinterpret_cast<hipStream_t>(stream));
@@ -763,14 +785,16 @@ namespace tide {
 
 tide_status issue_tiles_to_stage(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
                                  int64_t tile_count, float* stage, int32_t max_workgroups,
-                                 tide_stream_t stream) {
+                                 tide_stream_t stream, int64_t launch_tiles) {
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
     const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     int R = h.R;
     int64_t T = h.rs_tile;
     DenseKernel k = pick_dense(R, h.flags, h.rs_tile);
-    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
+    const int64_t per_launch = launch_tiles > 0         ? launch_tiles
+                               : h.rs_launch_tiles > 0 ? h.rs_launch_tiles
+                                                       : tile_count;
     for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
         const RsTile* tiles = all + b;
         int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch
@@ -850,6 +874,16 @@ extern "C" tide_status tide_rs_bf16_to_fp32_census(const void* h_plan, const voi
                                                    tide_stream_t stream) {
     if (!census) return TIDE_EINVAL;
     return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream, census, census_len);
+}
+
+extern "C" tide_status tide_rs_bf16_to_fp32_trace(const void* h_plan, const void* d_plan,
+                                                  int32_t order, int32_t max_workgroups,
+                                                  uint32_t* census, uint64_t* stamps,
+                                                  int64_t len, tide_stream_t stream) {
+    if (!census || !stamps) return TIDE_EINVAL;
+    if (reinterpret_cast<uintptr_t>(census) % 4 || reinterpret_cast<uintptr_t>(stamps) % 8)
+        return TIDE_EALIGN;
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream, census, len, stamps);
 }
 
 // ---- the two phases through the library's own staging array

@@ -74,3 +74,58 @@ class TwoPhase:
 
     def __exit__(self, *exc) -> None:
         self.close()
+
+
+def main(argv=None) -> int:
+    """Standalone pipelined runs on one layer, one phase-2 engine and a few
+    chunk sizes, for kernel traces: prints one JSON line per configuration
+    with the event time of a pipelined call (best of --reps), the host time
+    to issue it, and its bits against the in-place reduce-scatter."""
+    import argparse
+    import json
+    import time
+
+    from . import configs, harness
+
+    ap = argparse.ArgumentParser(description=main.__doc__)
+    ap.add_argument("--workload", default="2")
+    ap.add_argument("--phase2", default="cu", choices=("cu", "sdma"))
+    ap.add_argument("--phase2-cus", type=int, default=0)
+    ap.add_argument("--chunk-launches", default="1,4", help="chunk sizes in launches of the plan")
+    ap.add_argument("--depth", type=int, default=2)
+    ap.add_argument("--reps", type=int, default=2)
+    a = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        raise SystemExit("the pipeline needs a GPU")
+    w = configs.get(a.workload)
+    st = harness.setup(w, with_ag=False, guard=0)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.view(torch.int32).clone() for o in st.out]
+    L = int(st.plan.info.rs_launch_tiles) or int(st.plan.info.rs_tiles)
+    for mult in (float(x) for x in a.chunk_launches.split(",")):
+        chunk = max(1, int(L * mult))
+        with TwoPhase(st.plan, chunk, a.depth, a.phase2, a.phase2_cus) as tp:
+            tp.run()
+            torch.cuda.synchronize()
+            best, host = None, None
+            for _ in range(a.reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                h0 = time.perf_counter()
+                tp.run()
+                h1 = time.perf_counter()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                if best is None or ms < best:
+                    best, host = ms, (h1 - h0) * 1e3
+        same = all(torch.equal(r, o.view(torch.int32)) for r, o in zip(ref, st.out))
+        print(json.dumps({"workload": w.name, "phase2": a.phase2, "phase2_cus": a.phase2_cus,
+                          "chunk_tiles": chunk, "depth": a.depth, "ms": round(best, 3),
+                          "host_issue_ms": round(host, 3), "same_bits": same}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

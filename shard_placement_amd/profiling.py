@@ -221,8 +221,18 @@ def main(argv=None):
     o.add_argument("--logs", nargs="+", required=True, help="bench.py output of the same processes")
     o.add_argument("--command", required=True)
     o.add_argument("--title", required=True)
+    pp = sub.add_parser("pipeline")
+    pp.add_argument("out")
+    pp.add_argument("--dirs", nargs="+", required=True, help="kernel-trace folders, one per process")
+    pp.add_argument("--logs", nargs="+", required=True, help="output of the same processes")
+    pp.add_argument("--command", required=True)
+    pp.add_argument("--title", required=True)
     a = ap.parse_args(argv)
-    if a.cmd == "stats":
+    if a.cmd == "pipeline":
+        if len(a.dirs) != len(a.logs):
+            raise SystemExit("--dirs and --logs must pair up")
+        summarize_pipeline(a.dirs, a.logs, a.out, a.command, a.title)
+    elif a.cmd == "stats":
         summarize_stats(a.dir, a.out, a.command)
     elif a.cmd == "overlap":
         if len(a.dirs) != len(a.logs):
@@ -232,6 +242,120 @@ def main(argv=None):
         summarize_pmc(a.fetch_dir, a.write_dir, a.out, a.kernel, a.calib_kernel, a.calib_bytes,
                       a.algorithmic_bytes, a.src_hash, a.command_fetch, a.command_write, a.workload)
     return 0
+
+
+
+def cu_time(census, stamps, tick_hz: float = 1e8) -> dict:
+    """Compute-unit time a reduce-scatter held, from the per-tile trace of
+    tide_rs_bf16_to_fp32_trace: census[t] (packed CU id) and stamps[t] =
+    (start, end) in real-time counter ticks.  Per CU the union of its tiles'
+    intervals is the time it held at least one reduce-scatter workgroup; the
+    sum over CUs is the occupancy-weighted CU time (the one-GPU analog of the
+    pages' reduce-scatter "SM time").  Also the plain sum of workgroup
+    durations and the trace's span.  Inputs are numpy arrays (or anything
+    numpy can take)."""
+    import numpy as np
+
+    cu = np.asarray(census).astype(np.int64).reshape(-1)
+    st = np.asarray(stamps).astype(np.int64).reshape(-1, 2)
+    if cu.size == 0:
+        return {"cus": 0, "held_cu_ms": 0.0, "workgroup_ms_sum": 0.0, "span_ms": 0.0}
+    if np.any(st[:, 1] < st[:, 0]):
+        raise ValueError("a tile ends before it starts")
+    order = np.lexsort((st[:, 0], cu))
+    cu, st = cu[order], st[order]
+    held = 0
+    bounds = np.flatnonzero(np.diff(cu)) + 1
+    for s0, s1 in zip(np.r_[0, bounds], np.r_[bounds, cu.size]):
+        a, b = st[s0:s1, 0], st[s0:s1, 1]
+        prev_end = np.maximum.accumulate(np.r_[a[0], b[:-1]])
+        held += int(np.sum(np.maximum(0, b - np.maximum(a, prev_end))))
+    ms = 1e3 / tick_hz
+    return {"cus": int(np.unique(cu).size), "held_cu_ms": round(held * ms, 3),
+            "workgroup_ms_sum": round(float(np.sum(st[:, 1] - st[:, 0])) * ms, 3),
+            "span_ms": round(float(st[:, 1].max() - st[:, 0].min()) * ms, 4),
+            "tick_hz": tick_hz}
+
+
+def _union(iv):
+    """Total length of a union of (start, end) intervals, and the merged list."""
+    out, total = [], 0
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    for a, b in out:
+        total += b - a
+    return total, out
+
+
+def pipeline_phases(d: str, p1: str = "rs_dense_kernel", p2: str = "rs_drain_kernel") -> dict:
+    """From one process's kernel trace of pipelined runs: for the phase-1
+    (reduction into staging) and phase-2 (delivery into the arenas)
+    dispatches, the hardware queues and streams they ran on, how long each
+    phase kept the GPU busy (union of its dispatches), and how long both
+    ran at once (microseconds)."""
+    tr = kernel_trace(d)
+    rows = {1: [], 2: []}
+    for t in tr:
+        k = t.get("Kernel_Name", "")
+        ph = 1 if p1 in k else 2 if p2 in k else 0
+        if ph:
+            rows[ph].append((int(t["Start_Timestamp"]), int(t["End_Timestamp"]),
+                             t.get("Queue_Id"), t.get("Stream_Id")))
+    out = {}
+    merged = {}
+    for ph in (1, 2):
+        busy, merged[ph] = _union([(a, b) for a, b, _, _ in rows[ph]])
+        out["phase%d" % ph] = {"dispatches": len(rows[ph]),
+                               "queues": sorted({q for _, _, q, _ in rows[ph]}),
+                               "streams": sorted({s for _, _, _, s in rows[ph]}),
+                               "busy_us": round(busy / 1e3, 1)}
+    both = 0
+    i = j = 0
+    m1, m2 = merged[1], merged[2]
+    while i < len(m1) and j < len(m2):
+        lo, hi = max(m1[i][0], m2[j][0]), min(m1[i][1], m2[j][1])
+        if hi > lo:
+            both += hi - lo
+        if m1[i][1] < m2[j][1]:
+            i += 1
+        else:
+            j += 1
+    allr = rows[1] + rows[2]
+    span = (max(b for _, b, _, _ in allr) - min(a for a, _, _, _ in allr)) if allr else 0
+    out["both_busy_us"] = round(both / 1e3, 1)
+    out["span_us"] = round(span / 1e3, 1)
+    return out
+
+
+def summarize_pipeline(dirs, logs, out: str, command: str, title: str) -> None:
+    """One block per process: the run's own timing line and the phase
+    figures from its kernel trace."""
+    lines = ["# rocprofv3 kernel trace of the two-phase pipeline, %s" % title,
+             "command (one process each): %s" % command,
+             "per process: the pipeline's own timing (events), then from the kernel trace the",
+             "hardware queues and streams of phase 1 (rs_dense_kernel) and phase 2",
+             "(rs_drain_kernel), each phase's busy time (union of its dispatches), the time both",
+             "ran at once, and the span of all of them"]
+    for i, (d, lg) in enumerate(zip(dirs, logs), 1):
+        res = None
+        with open(lg) as fh:
+            for line in fh:
+                if line.startswith("{"):
+                    res = json.loads(line)
+        ph = pipeline_phases(d)
+        lines.append("")
+        lines.append("process %d: %s" % (i, json.dumps(res, sort_keys=True)))
+        for k in ("phase1", "phase2"):
+            v = ph[k]
+            lines.append("  %s: %d dispatches on queues %s, streams %s; busy %.1f us" % (
+                k, v["dispatches"], v["queues"], v["streams"], v["busy_us"]))
+        lines.append("  both phases at once: %.1f us of a %.1f us span" % (ph["both_busy_us"],
+                                                                        ph["span_us"]))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":

@@ -47,3 +47,45 @@ def test_overlap_summary_reads_the_probe_line(tmp_path):
     assert "512 tiles per launch, ? B of LDS per workgroup" in text and "(7.3%, 40 GEMMs inside)" in text
     assert "GEMMs overlapping the RS: 1; duration median 220 us" in text
     assert "launch ends inside a GEMM: median 1" in text
+
+
+def test_cu_time_union_per_cu():
+    from shard_placement_amd.profiling import cu_time
+
+    # CU 1: [0,10) and [5,20) overlap -> 20 ticks held; [30,35) -> 5 more
+    # CU 2: [0,4), [4,8) touch -> 8; nested [1,3) adds nothing
+    census = [1, 2, 1, 2, 1, 2]
+    stamps = [[0, 10], [0, 4], [5, 20], [4, 8], [30, 35], [1, 3]]
+    r = cu_time(census, stamps, tick_hz=1e3)  # 1 tick = 1 ms
+    assert r["cus"] == 2
+    assert r["held_cu_ms"] == 33.0
+    assert r["workgroup_ms_sum"] == 10 + 4 + 15 + 4 + 5 + 2
+    assert r["span_ms"] == 35.0
+
+
+def test_cu_time_rejects_reversed_intervals():
+    import pytest
+
+    from shard_placement_amd.profiling import cu_time
+
+    with pytest.raises(ValueError):
+        cu_time([0], [[5, 4]])
+
+
+def test_pipeline_phases_from_a_trace(tmp_path):
+    """Queues, busy time and time-both-busy from a made-up kernel trace."""
+    from shard_placement_amd.profiling import pipeline_phases
+
+    d = tmp_path / "run"
+    d.mkdir()
+    rows = [("rs_dense_kernel<8>", 3, 11, 0, 100), ("rs_drain_kernel<true>", 4, 12, 90, 150),
+            ("rs_dense_kernel<8>", 3, 11, 100, 200), ("rs_drain_kernel<true>", 4, 12, 200, 260),
+            ("Cijk_gemm", 1, 0, 0, 500)]
+    with open(d / "run_kernel_trace.csv", "w") as fh:
+        fh.write('"Kind","Queue_Id","Stream_Id","Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for k, q, s, a, b in rows:
+            fh.write('"KERNEL_DISPATCH",%d,%d,"%s",%d,%d\n' % (q, s, k, a * 1000, b * 1000))
+    r = pipeline_phases(str(d))
+    assert r["phase1"] == {"dispatches": 2, "queues": ["3"], "streams": ["11"], "busy_us": 200.0}
+    assert r["phase2"] == {"dispatches": 2, "queues": ["4"], "streams": ["12"], "busy_us": 120.0}
+    assert r["both_busy_us"] == 60.0 and r["span_us"] == 260.0
