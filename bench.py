@@ -136,7 +136,8 @@ def dma_placement_leg(st, agb: int) -> dict:
     del ref
     return {"engines": api.tide_dma_engine_count(), "ms": round(ms, 4),
             "GB/s": round(agb / (ms * 1e-3) / 1e9, 1), "same_bits": bool(same),
-            "copies": "one engine-pinned 1-D copy per (param, rank) run, host-synchronous"}
+            "copies": "one engine-pinned 1-D copy per (param, rank) run, host-synchronous",
+            "engine": "DMA engines through ROCr (no kernel is dispatched)"}
 
 
 def staged_leg(st, rsb: int, fused_ms: float, reps: int = 3) -> dict:
@@ -275,6 +276,9 @@ def pipeline_leg(st, fused_ms: float) -> dict:
             runs.append({"phase2": phase2, "chunk_tiles": chunk, "depth": depth,
                          "staging_mib": round(tp.staging_bytes / 2 ** 20, 1), "ms": round(t, 3),
                          "host_issue_ms": round(host_ms, 3),
+                         # the host needs about as long to issue the chunks
+                         # as the device to run them: the run is host-bound
+                         "host_bound": bool(host_ms >= 0.9 * t),
                          "overlap": round((serial - t) / min(t1, t2[phase2]), 3)})
             del tp
     del ref
@@ -514,11 +518,14 @@ def main():
 
     rsb, agb = harness.rs_bytes(w), harness.ag_bytes(w)
 
-    # Python's garbage collector stays paused from here on, as timeit does
-    # while timing: a collection pass inside a timed region once read as a
-    # +17..23% GEMM slowdown in the interference probe, and the host-timed
-    # legs (copy engines, pipeline issue) would absorb its pauses too.
+    # The heap is frozen after setup and the collector stays paused from here
+    # on, as timeit does while timing: a full collection walks every tracked
+    # object (~170 K here, ~20 ms of one core), and that walk alone, freeing
+    # nothing and making no HIP call, lengthened the single-wave GEMM by
+    # 10-15% in the interference probe; the host-timed legs (copy engines,
+    # pipeline issue) would absorb its pauses too.
     gc.collect()
+    gc.freeze()
     gc.disable()
 
     def step(ev=None):
@@ -600,7 +607,9 @@ def main():
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / reps
         sdma = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
-                "engine": "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run"}
+                "copies": "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run",
+                "engine": "chosen by the HIP runtime (DMA engines or blit kernels; not checked in "
+                          "this run: ag_dma is the path that never uses a compute unit)"}
         log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
 
     # which compute units the reduce-scatter ran on, and for how long (one

@@ -43,7 +43,6 @@ struct tide_pipeline {
     int device = -1;
     int32_t depth = 0;
     int32_t phase2_cus = 0;
-    int32_t ncu = 0;  // compute units of the device
     hipStream_t s1 = nullptr, s2 = nullptr;
     hipEvent_t start = nullptr, done1 = nullptr, done2 = nullptr;
     std::vector<hipEvent_t> produced, drained;
@@ -123,7 +122,6 @@ extern "C" tide_status tide_pipeline_create(int32_t depth, int32_t phase2_cus,
     p->device = dev;
     p->depth = depth;
     p->phase2_cus = phase2_cus;
-    p->ncu = ncu;
     // phase 2 confined to CUs [0, phase2_cus), phase 1 to the rest; with
     // phase2_cus == 0 both streams may use every CU
     tide_stream_t s1 = nullptr, s2 = nullptr;
@@ -179,17 +177,6 @@ extern "C" tide_status tide_pipeline_run(tide_pipeline_t p, const void* h_plan,
     const uint64_t lo = reinterpret_cast<uint64_t>(ring);
     if (overlaps_rs_buffers(h_plan, lo, lo + 4ull * (uint64_t)need)) return TIDE_EOVERLAP;
 
-    // Phase 1's launches keep the plan's workgroups per compute unit on the
-    // CUs its stream may use.  At R = 64 the default launch holds exactly two
-    // workgroups per CU of the device, and its LDS reservation lets no more
-    // than two share a CU; with phase 2 on k CUs (the mask takes them from
-    // every XCD alike) a launch of the plan's size would leave k/8 * 2
-    // workgroups per XCD for a second round.
-    int64_t launch1 = 0;
-    if (p->phase2_cus > 0 && h.rs_launch_tiles > 0 && p->ncu > 0) {
-        launch1 = h.rs_launch_tiles * (p->ncu - p->phase2_cus) / p->ncu;
-        if (launch1 < 1) launch1 = 1;
-    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     tide_stream_t s1 = reinterpret_cast<tide_stream_t>(p->s1);
     tide_stream_t s2 = reinterpret_cast<tide_stream_t>(p->s2);
@@ -206,7 +193,7 @@ extern "C" tide_status tide_pipeline_run(tide_pipeline_t p, const void* h_plan,
             break;
         }
         // the ring and the tile range were checked above, once for all chunks
-        st = issue_tiles_to_stage(h, d_plan, b, cnt, buf, 0, s1, launch1);
+        st = issue_tiles_to_stage(h, d_plan, b, cnt, buf, 0, s1);
         if (st != TIDE_OK) break;
         if (hipEventRecord(p->produced[k], p->s1) != hipSuccess ||
             hipStreamWaitEvent(p->s2, p->produced[k], 0) != hipSuccess) {

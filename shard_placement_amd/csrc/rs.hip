@@ -785,16 +785,14 @@ namespace tide {
 
 tide_status issue_tiles_to_stage(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
                                  int64_t tile_count, float* stage, int32_t max_workgroups,
-                                 tide_stream_t stream, int64_t launch_tiles) {
+                                 tide_stream_t stream) {
     const uint8_t* d = static_cast<const uint8_t*>(d_plan);
     const RsTile* all = reinterpret_cast<const RsTile*>(d + h.off_rs);
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     int R = h.R;
     int64_t T = h.rs_tile;
     DenseKernel k = pick_dense(R, h.flags, h.rs_tile);
-    const int64_t per_launch = launch_tiles > 0         ? launch_tiles
-                               : h.rs_launch_tiles > 0 ? h.rs_launch_tiles
-                                                       : tile_count;
+    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
     for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
         const RsTile* tiles = all + b;
         int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch

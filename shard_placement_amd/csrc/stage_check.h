@@ -37,11 +37,9 @@ tide_status check_pipeline(const void* h_plan, const void* d_plan, int64_t tile_
 // have validated the plan, the tile range and the staging memory already
 // (the pipeline driver checks its whole ring once, then issues chunk by
 // chunk).  h is the plan's header.
-// launch_tiles > 0 replaces the plan's tiles per launch (the pipeline sizes
-// phase 1's launches to the compute units its stream may use).
 tide_status issue_tiles_to_stage(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
                                  int64_t tile_count, float* stage, int32_t max_workgroups,
-                                 tide_stream_t stream, int64_t launch_tiles = 0);
+                                 tide_stream_t stream);
 tide_status issue_stage_to_shards(const PlanHeader& h, const void* d_plan, int64_t tile_begin,
                                   int64_t tile_count, const float* stage, int32_t max_workgroups,
                                   tide_stream_t stream);

@@ -37,17 +37,27 @@ def _median(xs: List[float]) -> Optional[float]:
 
 @contextlib.contextmanager
 def _no_gc():
-    """The Python garbage collector paused (after one collection), as
-    Python's timeit does while timing.  Measured on the R = 64 layer: a
-    collection pass inside the concurrent window read +17..23% GEMM slowdown
-    where the same process with the collector paused, or collected just
-    before, read +2..7%."""
+    """The heap frozen and the collector paused while timing.
+
+    A full collection walks every tracked Python object (about 170 K in a
+    process holding torch and this package: 18-24 ms of one core).  Measured
+    on the R = 64 layer with a side thread collecting every 20 ms during the
+    probe: the walk alone, with nothing to free and no HIP call made by the
+    collecting thread, stretched the single-wave GEMM from 0.20 to 0.23-0.24
+    ms, alone and beside the reduce-scatter (+14.5..17% instead of
+    +3.6..3.8%).  After gc.freeze() the same collections take 0.02 ms and
+    the reading is the quiet one (+3.2..4.8%).  So the heap is frozen here
+    (any collection in the window has almost nothing to walk), and the
+    collector is also paused, as Python's timeit does; both are restored on
+    exit."""
     was = gc.isenabled()
     gc.collect()
+    gc.freeze()
     gc.disable()
     try:
         yield
     finally:
+        gc.unfreeze()
         if was:
             gc.enable()
 
@@ -64,14 +74,17 @@ def _gemm_train(a, b, c, stream, n):
 
 
 def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N: int = 4096,
-        K: int = 8192) -> Dict:
+        K: int = 8192, quiet_gc: bool = True) -> Dict:
     """Time the GEMM alone, then, per mode, alone again and beside the
     mode's reduce-scatter (the slowdown is against the mode's own alone
     time).  The
     reduce-scatter always runs on a CU-masked stream, which HIP backs with a
     hardware queue of its own (with the full mask when the mode has none):
     two streams that share a hardware queue run one after the other, which
-    would hide any interference.  The garbage collector is paused meanwhile."""
+    would hide any interference.  The heap is frozen and the garbage
+    collector paused meanwhile (quiet_gc=False leaves both alone)."""
+    if not quiet_gc:
+        return _run(modes, rs_bytes, iters, M, N, K)
     with _no_gc():
         return _run(modes, rs_bytes, iters, M, N, K)
 
@@ -196,21 +209,85 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="5", help="workload key or name")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--iters", type=int, default=40)
+    ap.add_argument("--side", default="none", choices=("none", "collect", "collect-frozen", "trim"),
+                    help="a side thread acting every 20 ms during the probe: a full garbage "
+                         "collection, the same after gc.freeze(), or malloc_trim(0)")
     a = ap.parse_args(argv)
     if not torch.cuda.is_available():
         raise SystemExit("the probe needs a GPU")
     w = configs.get(a.workload)
     st = harness.setup(w, with_ag=False)
     torch.cuda.synchronize()
+    side = _Side(a.side)
     res = None
     for _ in range(a.reps):
-        r = run([("default launches", st.plan, 0, 0)], harness.rs_bytes(w), iters=a.iters)
+        r = run([("default launches", st.plan, 0, 0)], harness.rs_bytes(w), iters=a.iters,
+                 quiet_gc=a.side == "none")
         if res is None:
             res = r
         else:
             res["modes"] += r["modes"]
-    print(json.dumps({"workload": w.name, "R": w.R, "probe": res}), flush=True)
+    side.stop()
+    print(json.dumps({"workload": w.name, "R": w.R, "side": side.report(), "probe": res}),
+          flush=True)
     return 0
+
+
+class _Side:
+    """A thread that, every 20 ms until stopped, runs a full garbage
+    collection ("collect"), the same after freezing the heap once
+    ("collect-frozen"), or glibc's malloc_trim(0) ("trim"); collections are
+    logged through gc.callbacks."""
+
+    def __init__(self, mode: str):
+        import ctypes
+        import threading
+        import time
+
+        self.mode, self.took, self.log = mode, [], []
+        self._t0 = 0.0
+        gc.callbacks.append(self._cb)
+        if mode == "collect-frozen":
+            gc.collect()
+            gc.freeze()
+        self._stop = threading.Event()
+        libc = ctypes.CDLL("libc.so.6") if mode == "trim" else None
+
+        def loop():
+            while not self._stop.is_set():
+                time.sleep(0.02)
+                t = time.perf_counter()
+                if mode in ("collect", "collect-frozen"):
+                    gc.collect()
+                elif mode == "trim":
+                    libc.malloc_trim(0)
+                self.took.append(time.perf_counter() - t)
+        self._th = threading.Thread(target=loop, daemon=True)
+        if mode != "none":
+            self._th.start()
+
+    def _cb(self, phase, info):
+        import time
+
+        if phase == "start":
+            self._t0 = time.perf_counter()
+        else:
+            self.log.append((info["generation"], info["collected"], time.perf_counter() - self._t0))
+
+    def stop(self):
+        self._stop.set()
+        if self._th.is_alive():
+            self._th.join()
+        gc.callbacks.remove(self._cb)
+        if self.mode == "collect-frozen":
+            gc.unfreeze()
+
+    def report(self) -> Dict:
+        return {"mode": self.mode, "calls": len(self.took),
+                "call_ms_mean": round(1e3 * sum(self.took) / max(1, len(self.took)), 3),
+                "collections": len(self.log),
+                "objects_freed": sum(c for _, c, _ in self.log),
+                "tracked_objects": len(gc.get_objects())}
 
 
 if __name__ == "__main__":

@@ -32,3 +32,29 @@ def test_standalone_probe_needs_a_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(SystemExit, match="needs a GPU"):
         probe.main(["--workload", "1"])
+
+
+def test_timed_regions_freeze_the_heap():
+    """Inside the window a collection has (almost) nothing to walk; the heap
+    is unfrozen again on exit."""
+    junk = [[i] for i in range(1000)]  # tracked containers
+    before = gc.get_freeze_count()
+    with probe._no_gc():
+        assert gc.get_freeze_count() >= len(junk)
+        assert len(gc.get_objects()) < 1000
+    assert gc.get_freeze_count() == before
+    assert len(junk) == 1000
+
+
+def test_side_thread_collects_and_reports():
+    import time
+
+    s = probe._Side("collect")
+    time.sleep(0.1)
+    s.stop()
+    r = s.report()
+    assert r["mode"] == "collect" and r["calls"] >= 1 and r["collections"] >= 1
+    assert r["tracked_objects"] > 0
+    s = probe._Side("none")
+    s.stop()
+    assert s.report()["calls"] == 0
