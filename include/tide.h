@@ -355,7 +355,10 @@ tide_status tide_rs_stage_to_shards_sdma(const void *h_plan, int64_t tile_begin,
 tide_status tide_stream_create_cu_limited(int32_t n_cu, tide_stream_t *out);
 /* The same for the mask bits [first_cu, first_cu + n_cu): two streams with
  * disjoint ranges never share a compute unit.  first_cu >= 0, n_cu >= 1,
- * first_cu + n_cu <= number of CUs. */
+ * first_cu + n_cu <= number of CUs.  On MI355X consecutive mask bits go to
+ * the 8 XCDs in turn (bits [0, 8) are one CU on each XCD), and the runtime
+ * refused masks of a single CU (TIDE_EHIP) while masks of 8, 16, 32, 64 and
+ * 248 CUs worked. */
 tide_status tide_stream_create_cu_range(int32_t first_cu, int32_t n_cu, tide_stream_t *out);
 tide_status tide_stream_destroy(tide_stream_t stream);
 
