@@ -455,6 +455,7 @@ def test_full_size_workload(key):
     torch.cuda.synchronize()
     gu.check_rs_sampled(st, order="tree", per_shard=32, edge=8, seed=1)
     gu.check_rs_bound_all(st, order="tree")
+    assert gu.check_rs_whole(st, order="tree") == w.numel()
     st.plan.rs()
     torch.cuda.synchronize()
     # determinism at full size
