@@ -40,7 +40,22 @@ def kernel_trace(d: str):
         return list(csv.DictReader(fh))
 
 
-def summarize_stats(d: str, out: str, command: str, top: int = 12) -> None:
+def idle_stretches(trace, n: int = 3):
+    """The n longest stretches of a kernel trace with no dispatch running
+    (between the end of the last dispatch so far and the start of the
+    next), as (length, start, end) in ms from the first dispatch."""
+    iv = sorted((int(t["Start_Timestamp"]), int(t["End_Timestamp"])) for t in trace)
+    if not iv:
+        return []
+    t0, reach, gaps = iv[0][0], iv[0][1], []
+    for a, b in iv[1:]:
+        if a > reach:
+            gaps.append(((a - reach) / 1e6, (reach - t0) / 1e6, (a - t0) / 1e6))
+        reach = max(reach, b)
+    return sorted(gaps, reverse=True)[:n]
+
+
+def summarize_stats(d: str, out: str, command: str, top: int = 12, gaps: int = 0) -> None:
     rows = kernel_stats(d)
     rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
     lines = ["# rocprofv3 kernel statistics", "command: %s" % command,
@@ -66,6 +81,11 @@ def summarize_stats(d: str, out: str, command: str, top: int = 12) -> None:
                 t.get("VGPR_Count", t.get("Arch_VGPR_Count", "?")), t.get("SGPR_Count", "?"),
                 t.get("LDS_Block_Size", t.get("Lds_Size", "?")),
                 t.get("Scratch_Size", "?")))
+        if gaps:
+            lines.append("")
+            lines.append("# the longest stretches with no kernel dispatch running (ms from the first dispatch)")
+            for g, a, b in idle_stretches(tr, gaps):
+                lines.append("no dispatch for %.1f ms: %.3f .. %.3f ms" % (g, a, b))
     except FileNotFoundError:
         pass
     with open(out, "w") as fh:
@@ -203,6 +223,7 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("out")
     s.add_argument("--command", required=True)
+    s.add_argument("--gaps", type=int, default=0, help="also list the N longest idle stretches")
     p = sub.add_parser("pmc")
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
@@ -233,7 +254,7 @@ def main(argv=None):
             raise SystemExit("--dirs and --logs must pair up")
         summarize_pipeline(a.dirs, a.logs, a.out, a.command, a.title)
     elif a.cmd == "stats":
-        summarize_stats(a.dir, a.out, a.command)
+        summarize_stats(a.dir, a.out, a.command, gaps=a.gaps)
     elif a.cmd == "overlap":
         if len(a.dirs) != len(a.logs):
             raise SystemExit("--dirs and --logs must pair up")

@@ -89,3 +89,13 @@ def test_pipeline_phases_from_a_trace(tmp_path):
     assert r["phase1"] == {"dispatches": 2, "queues": ["3"], "streams": ["11"], "busy_us": 200.0}
     assert r["phase2"] == {"dispatches": 2, "queues": ["4"], "streams": ["12"], "busy_us": 120.0}
     assert r["both_busy_us"] == 60.0 and r["span_us"] == 260.0
+
+
+def test_idle_stretches():
+    from shard_placement_amd.profiling import idle_stretches
+
+    ms = 1_000_000
+    tr = [{"Start_Timestamp": a * ms, "End_Timestamp": b * ms}
+          for a, b in [(0, 10), (5, 12), (40, 50), (50, 51), (200, 210), (60, 70)]]
+    assert idle_stretches(tr, 2) == [(130.0, 70.0, 200.0), (28.0, 12.0, 40.0)]
+    assert idle_stretches([], 3) == []
