@@ -221,13 +221,18 @@ class BlockReader:
             return
         spans = [(a, min(n, a + self.block)) for a in range(0, n, self.block)]
         pending = self._issue(0, p, *spans[0])
-        for i, (a, b) in enumerate(spans):
-            k = i & 1
-            t0 = time.perf_counter()
+        try:
+            for i, (a, b) in enumerate(spans):
+                k = i & 1
+                t0 = time.perf_counter()
+                pending.synchronize()
+                self.copy_s += time.perf_counter() - t0
+                if i + 1 < len(spans):
+                    pending = self._issue(k ^ 1, p, *spans[i + 1])
+                L = b - a
+                g = [self.g[k][q, :L].numpy().view(np.uint16) for q in range(self.st.w.R)]
+                yield a, b, g, self.o[k][:L].numpy().view(np.uint32)
+        finally:
+            # a caller that stops early (an exception, a break) must not free
+            # the pinned buffers under a copy that is still writing them
             pending.synchronize()
-            self.copy_s += time.perf_counter() - t0
-            if i + 1 < len(spans):
-                pending = self._issue(k ^ 1, p, *spans[i + 1])
-            L = b - a
-            g = [self.g[k][q, :L].numpy().view(np.uint16) for q in range(self.st.w.R)]
-            yield a, b, g, self.o[k][:L].numpy().view(np.uint32)
