@@ -401,6 +401,52 @@ def cpu_baseline(st, budget_s: float) -> dict:
     }
 
 
+def two_queue_leg(st, rsb: int, fused_ms: float, probe_on: bool = True, reps: int = 10) -> dict:
+    """The reduce-scatter with its launches dealt over two hardware queues
+    (the current stream and a CU-masked stream of all CUs): its rate alone,
+    its bits against the one-queue result, and the single-wave GEMM beside
+    it (the launch boundaries that let a concurrent GEMM in are mostly
+    lost)."""
+    import torch
+
+    from shard_placement_amd import api, probe
+
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    # two CU-masked streams of all CUs, each with a hardware queue of its own
+    # (not the null stream, which would serialise the launches)
+    main = api.tide_stream_create_cu_limited(n_cu)
+    extra = api.tide_stream_create_cu_limited(n_cu)
+    try:
+        st.plan.rs()
+        torch.cuda.synchronize()
+        ref = [o.view(torch.int32).clone() for o in st.out]
+        st.plan.rs_streams([extra], stream=main)
+        torch.cuda.synchronize()
+        same = all(torch.equal(r, o.view(torch.int32)) for r, o in zip(ref, st.out))
+        del ref
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        for _ in range(reps):
+            st.plan.rs_streams([extra], stream=main)
+        e1.record(main)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rec = {"queues": 2, "rs_ms": round(ms, 4), "rs_gbps": round(rsb / (ms * 1e-3) / 1e9, 1),
+               "rs_frac_hbm": round(rsb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "one_queue_rs_ms": round(fused_ms, 4), "same_bits": bool(same)}
+        if probe_on:
+            m = probe.run([("launches dealt over two queues", probe.DealtRS(st.plan, [extra]), 0, 0)],
+                          rsb, iters=40)["modes"][0]
+            rec.update({"t_gemm_alone_ms": m["t_gemm_alone_ms"],
+                        "t_gemm_concurrent_ms": m["t_gemm_concurrent_ms"],
+                        "gemm_slowdown_pct": m["gemm_slowdown_pct"]})
+    finally:
+        torch.cuda.synchronize()
+        api.tide_stream_destroy(extra)
+        api.tide_stream_destroy(main)
+    return rec
+
+
 def others_leg(keys, args, reps: int = 10) -> dict:
     """RS and AG rates of other workloads in the default launch
     configuration (event time on the launch stream, after two warm-up
@@ -474,6 +520,8 @@ def main():
                     help="skip the two-phase pipeline emulation leg")
     ap.add_argument("--no-stock", action="store_true",
                     help="skip timing the stock-FSDP2 analog (pack, add, copy out in torch ops)")
+    ap.add_argument("--no-two-queues", action="store_true",
+                    help="skip the two-queue leg (launches dealt over two hardware queues)")
     ap.add_argument("--no-trace", action="store_true",
                     help="skip the traced call (CU census and per-tile timing)")
     ap.add_argument("--others", default="2,3,4",
@@ -683,6 +731,11 @@ def main():
             log("probe", m)
         del modes
 
+    two_q = None
+    if not args.no_two_queues:
+        two_q = two_queue_leg(st, rsb, rs_avg, probe_on=not args.no_probe)
+        log("two queues", two_q)
+
     traffic_ratio = read_traffic("rs_fixed_kernel", w.name, RS_SOURCES)
     cpu = None
     if not args.no_cpu_baseline:
@@ -738,6 +791,7 @@ def main():
         "staged_rs": staged_rec,
         "pipeline": pipe_rec,
         "stock_analog": stock_rec,
+        "rs_two_queues": two_q,
         "probe": probe,
         # per kernel launch: one reduce-scatter call is n_launch launches of
         # about rsb / n_launch algorithmic bytes; the event time per call

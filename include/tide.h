@@ -208,6 +208,24 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
                                        int64_t tile_count, int32_t max_workgroups,
                                        tide_stream_t stream);
 
+/* The same launches dealt over n_streams streams in turn (launch i on
+ * streams[i % n_streams]), so that with streams on different hardware queues
+ * (e.g. from tide_stream_create_cu_limited) a launch can start on the CUs the
+ * previous one is vacating instead of waiting for it to drain.  Same results.
+ * Measured on MI355X with two queues: 6.46-6.54 TB/s against 5.99 on the
+ * R = 64 layer, 5.92-6.08 against 5.58 on the R = 16 MoE layer, none on the
+ * R = 8 layer; but a concurrent single-wave GEMM then loses the launch
+ * boundaries that let it in (+12..88% against +2..6%): a mode for when no
+ * compute runs beside the reduce-scatter.  The caller orders the streams
+ * against its other work (e.g. the others wait for an event of the first,
+ * the first waits for events of the others).  n_streams in [1, 64]; with
+ * more than one stream none may be the null stream (TIDE_EINVAL: it
+ * synchronises with every blocking stream, which would serialise the
+ * launches; measured 72 ms against 19 ms for one stream). */
+tide_status tide_rs_bf16_to_fp32_streams(const void *h_plan, const void *d_plan,
+                                         int32_t order, int32_t max_workgroups,
+                                         const tide_stream_t *streams, int32_t n_streams);
+
 /* The reduce-scatter of tide_rs_bf16_to_fp32 (same launches, same
  * results) that also records, for every tile t of the plan, the compute
  * unit that processed it: census[t] = xcc_id << 8 | se_id << 5 | sh_id << 4

@@ -28,7 +28,8 @@ EXPORTS = ("tide_abi_version", "tide_status_str", "tide_desc_size", "tide_desc_g
            "tide_rs_stage_dma", "tide_rs_fold_staged", "tide_rs_tiles_to_stage",
            "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles",
            "tide_stream_create_cu_range", "tide_pipeline_create", "tide_pipeline_run",
-           "tide_pipeline_destroy", "tide_rs_two_phase_noalloc", "tide_rs_bf16_to_fp32_trace")
+           "tide_pipeline_destroy", "tide_rs_two_phase_noalloc", "tide_rs_bf16_to_fp32_trace",
+           "tide_rs_bf16_to_fp32_streams")
 
 
 class TideShape(ctypes.Structure):
@@ -116,6 +117,7 @@ def lib():
     L.tide_pipeline_destroy.argtypes = [vp]
     L.tide_rs_two_phase_noalloc.argtypes = [vp, vp, i64, i64, i32, vp]
     L.tide_rs_bf16_to_fp32_trace.argtypes = [vp, vp, i32, i32, vp, vp, i64, vp]
+    L.tide_rs_bf16_to_fp32_streams.argtypes = [vp, vp, i32, i32, ctypes.POINTER(vp), i32]
     for name in ("tide_desc_size", "tide_desc_geometry", "tide_desc_build", "tide_plan_query",
                  "tide_rs_bf16_to_fp32", "tide_ag_place", "tide_ag_place_sdma",
                  "tide_stream_create_cu_limited", "tide_stream_destroy",
@@ -125,7 +127,7 @@ def lib():
                  "tide_rs_stage_to_shards", "tide_rs_stage_to_shards_sdma", "tide_plan_rank_tiles",
                  "tide_stream_create_cu_range", "tide_pipeline_create", "tide_pipeline_run",
                  "tide_pipeline_destroy", "tide_rs_two_phase_noalloc",
-                 "tide_rs_bf16_to_fp32_trace"):
+                 "tide_rs_bf16_to_fp32_trace", "tide_rs_bf16_to_fp32_streams"):
         getattr(L, name).restype = ctypes.c_int
     if L.tide_abi_version() != 2:
         raise RuntimeError("libtide ABI version %d, expected 2" % L.tide_abi_version())

@@ -128,6 +128,16 @@ def tide_rs_bf16_to_fp32_tiles(h_plan: np.ndarray, d_plan: torch.Tensor, order: 
           "tide_rs_bf16_to_fp32_tiles")
 
 
+def tide_rs_bf16_to_fp32_streams(h_plan: np.ndarray, d_plan: torch.Tensor, streams,
+                                 order: int = 0, max_workgroups: int = 0) -> None:
+    """The reduce-scatter's launches dealt over ``streams`` in turn (the
+    caller orders the streams against its other work)."""
+    arr = (ctypes.c_void_p * len(streams))(*[int(s.cuda_stream) for s in streams])
+    check(_lib.lib().tide_rs_bf16_to_fp32_streams(h_plan.ctypes.data, d_plan.data_ptr(), int(order),
+                                                  int(max_workgroups), arr, len(streams)),
+          "tide_rs_bf16_to_fp32_streams")
+
+
 def tide_rs_bf16_to_fp32_census(h_plan: np.ndarray, d_plan: torch.Tensor, census: torch.Tensor,
                                 order: int = 0, max_workgroups: int = 0, stream=None) -> None:
     if census.dtype != torch.int32 or census.device.type != "cuda" or not census.is_contiguous():
@@ -372,6 +382,23 @@ class Plan:
 
     def rs(self, order: str = "fixed", max_workgroups: int = 0, stream=None) -> None:
         tide_rs_bf16_to_fp32(self.blob, self.d_blob, ORDERS[order], max_workgroups, stream)
+
+    def rs_streams(self, streams, order: str = "fixed", max_workgroups: int = 0,
+                   stream=None) -> None:
+        """The reduce-scatter with its launches dealt over ``stream`` (default:
+        the current stream) and the extra ``streams`` in turn, ordered after
+        ``stream``'s earlier work and before its later work (events)."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(main)
+        for s in streams:
+            s.wait_event(start)
+        tide_rs_bf16_to_fp32_streams(self.blob, self.d_blob, [main] + list(streams),
+                                     ORDERS[order], max_workgroups)
+        for s in streams:
+            done = torch.cuda.Event()
+            done.record(s)
+            main.wait_event(done)
 
     def rs_chunked(self, chunk_tiles: int, order: str = "fixed", max_workgroups: int = 0,
                    stream=None) -> int:

@@ -679,9 +679,11 @@ unsigned rs_extra_lds(const PlanHeader& h) {
     return h.rs_lds_bytes > (uint32_t)kRsStaticLds ? h.rs_lds_bytes - (uint32_t)kRsStaticLds : 0u;
 }
 
+// Launch i of the call goes to streams[i % n_streams] (one stream unless a
+// caller deals the launches over several hardware queues).
 tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int64_t tile_begin,
-                      int64_t tile_count, int32_t max_workgroups, tide_stream_t stream,
-                      uint32_t* census = nullptr, int64_t census_len = 0,
+                      int64_t tile_count, int32_t max_workgroups, const tide_stream_t* streams,
+                      int32_t n_streams, uint32_t* census = nullptr, int64_t census_len = 0,
                       uint64_t* stamps = nullptr) {
     if (!h_plan || !d_plan) return TIDE_EINVAL;
     PlanHeader h;
@@ -708,7 +710,8 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
 
     // One launch per run of per_launch tiles: the launch boundaries are where
     // kernels on other hardware queues get whole compute units.
-    for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
+    int64_t i = 0;
+    for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch, ++i) {
         const RsTile* tiles = all + b;
         int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch
                                                                   : tile_begin + tile_count - b;
@@ -720,7 +723,7 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         void* args[] = {&tiles, &ntiles, &gptr, &obase, &R, &cen, &stp};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
                                        dim3(kBlock), args, rs_extra_lds(h),
-                                       reinterpret_cast<hipStream_t>(stream));
+                                       reinterpret_cast<hipStream_t>(streams[i % n_streams]));
         if (e != hipSuccess) return TIDE_EHIP;
     }
     return TIDE_OK;
@@ -730,7 +733,20 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
 
 extern "C" tide_status tide_rs_bf16_to_fp32(const void* h_plan, const void* d_plan, int32_t order,
                                             int32_t max_workgroups, tide_stream_t stream) {
-    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream);
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, &stream, 1);
+}
+
+extern "C" tide_status tide_rs_bf16_to_fp32_streams(const void* h_plan, const void* d_plan,
+                                                    int32_t order, int32_t max_workgroups,
+                                                    const tide_stream_t* streams,
+                                                    int32_t n_streams) {
+    if (!streams || n_streams < 1 || n_streams > 64) return TIDE_EINVAL;
+    // the null stream waits for (and holds up) every blocking stream: dealing
+    // launches between it and other streams would serialise them all
+    if (n_streams > 1)
+        for (int32_t i = 0; i < n_streams; ++i)
+            if (!streams[i]) return TIDE_EINVAL;
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, streams, n_streams);
 }
 
 extern "C" tide_status tide_rs_bf16_to_fp32_tiles(const void* h_plan, const void* d_plan,
@@ -738,7 +754,7 @@ extern "C" tide_status tide_rs_bf16_to_fp32_tiles(const void* h_plan, const void
                                                   int64_t tile_count, int32_t max_workgroups,
                                                   tide_stream_t stream) {
     if (tile_count < 0) return TIDE_EINVAL;
-    return launch_rs(h_plan, d_plan, order, tile_begin, tile_count, max_workgroups, stream);
+    return launch_rs(h_plan, d_plan, order, tile_begin, tile_count, max_workgroups, &stream, 1);
 }
 
 extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_plan, int32_t order,
@@ -871,7 +887,7 @@ extern "C" tide_status tide_rs_bf16_to_fp32_census(const void* h_plan, const voi
                                                    uint32_t* census, int64_t census_len,
                                                    tide_stream_t stream) {
     if (!census) return TIDE_EINVAL;
-    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream, census, census_len);
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, &stream, 1, census, census_len);
 }
 
 extern "C" tide_status tide_rs_bf16_to_fp32_trace(const void* h_plan, const void* d_plan,
@@ -881,7 +897,7 @@ extern "C" tide_status tide_rs_bf16_to_fp32_trace(const void* h_plan, const void
     if (!census || !stamps) return TIDE_EINVAL;
     if (reinterpret_cast<uintptr_t>(census) % 4 || reinterpret_cast<uintptr_t>(stamps) % 8)
         return TIDE_EALIGN;
-    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, stream, census, len, stamps);
+    return launch_rs(h_plan, d_plan, order, 0, -1, max_workgroups, &stream, 1, census, len, stamps);
 }
 
 // ---- the two phases through the library's own staging array

@@ -62,6 +62,17 @@ def _no_gc():
             gc.enable()
 
 
+class DealtRS:
+    """A mode's reduce-scatter with its launches dealt over the probe's
+    stream and ``extra`` streams in turn (tide_rs_bf16_to_fp32_streams)."""
+
+    def __init__(self, plan, extra):
+        self.plan, self.extra, self.info = plan, list(extra), plan.info
+
+    def rs(self, max_workgroups: int = 0, stream=None) -> None:
+        self.plan.rs_streams(self.extra, max_workgroups=max_workgroups, stream=stream)
+
+
 def _gemm_train(a, b, c, stream, n):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]

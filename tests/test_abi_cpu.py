@@ -593,3 +593,25 @@ def test_noalloc_two_phase_validates_before_touching_the_gpu():
     assert call(b=n - cap - 1, cnt=cap + 1) == -4
     assert call(dev=ctypes.c_void_p((1 << 44) + 8)) == -2
     assert call(cnt=0) == 0 and call(b=n, cnt=0) == 0   # nothing to do
+
+
+def test_streams_variant_validates_before_touching_the_gpu():
+    R = 4
+    _, _, _, S = api.tide_desc_geometry(SHAPES, R)
+    g, o, ga, f = _fake_ptrs(SHAPES, R, S)
+    L = _lib.lib()
+    blob, _ = api.tide_desc_build(SHAPES, R, g, o, None, None)
+    fake_dev = ctypes.c_void_p(1 << 44)
+    vp = ctypes.c_void_p
+    two = (vp * 2)(1 << 20, 2 << 20)                                   # made-up handles
+    F = L.tide_rs_bf16_to_fp32_streams
+    assert F(blob.ctypes.data, fake_dev, 0, 0, (vp * 2)(None, 2 << 20), 2) == -1  # null stream
+    assert F(blob.ctypes.data, fake_dev, 0, 0, (vp * 2)(1 << 20, None), 2) == -1
+    assert F(blob.ctypes.data, fake_dev, 0, 0, None, 1) == -1          # no stream array
+    assert F(blob.ctypes.data, fake_dev, 0, 0, two, 0) == -1           # no stream
+    assert F(blob.ctypes.data, fake_dev, 0, 0, two, 65) == -1          # too many
+    assert F(blob.ctypes.data, fake_dev, 2, 0, two, 2) == -1           # bad order
+    assert F(blob.ctypes.data, ctypes.c_void_p((1 << 44) + 8), 0, 0, two, 2) == -2
+    assert F(np.zeros(4096, np.uint8).ctypes.data, fake_dev, 0, 0, two, 2) == -7
+    ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
+    assert F(ag_blob.ctypes.data, fake_dev, 0, 0, two, 2) == -6

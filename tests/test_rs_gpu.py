@@ -350,6 +350,34 @@ def test_cu_census_same_bits_and_counts():
         api.tide_stream_destroy(s)
 
 
+@pytest.mark.parametrize("R,shapes", [(8, [(4096, 256), (7,), (130, 24)]),
+                                      (64, [(4096, 1024), (1001, 64), (128,)])], ids=["8", "64"])
+def test_launches_dealt_over_streams_same_bits(R, shapes):
+    """tide_rs_bf16_to_fp32_streams: the launches over 1, 2 or 3 CU-masked
+    streams (hardware queues of their own) give the oracle's bits."""
+    w = _wl(shapes, R, key=175 + R, sigma=1e-3)
+    st = harness.setup(w, with_ag=False, guard=64, launch_mib=8)
+    assert -(-int(st.plan.info.rs_tiles) // int(st.plan.info.rs_launch_tiles)) >= 3
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    extra = [api.tide_stream_create_cu_limited(ncu) for _ in range(3)]
+    try:
+        for k in (0, 1, 2):
+            for o in st.out_alloc:
+                o.view(torch.int32).fill_(-1)
+            torch.cuda.synchronize()
+            gu.say("rs over", k + 1, "streams, R", R)
+            st.plan.rs_streams(extra[1:1 + k], stream=extra[0])
+            torch.cuda.synchronize()
+            gu.check_rs_full(st)
+        # dealing launches onto the null stream is refused
+        with pytest.raises(api.TideError):
+            st.plan.rs_streams(extra[:1])
+    finally:
+        torch.cuda.synchronize()
+        for s in extra:
+            api.tide_stream_destroy(s)
+
+
 def test_cu_limited_stream_bounds():
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     with pytest.raises(api.TideError):
