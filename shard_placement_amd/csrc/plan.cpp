@@ -54,9 +54,11 @@ constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 // R = 64 a 160 MiB launch would hold 620 tiles, 2.4 per CU, which leaves
 // the waves unbalanced (5.6 TB/s), while 512 tiles (132 MiB) read 6.01
 // TB/s against 6.12 at 1024 and cut the GEMM's slowdown from +11..15% to
-// +3..10%.  Placement: 256 MiB (its own interference is not what the
-// probe measures, and shorter launches cost it 4%).  An explicit launch
-// size applies to both, unrounded.
+// +3..10%.  Placement: 256 MiB, the same trade: beside the single-wave
+// GEMM (Llama-3.1-70B layer, three runs each) 256 MiB launches cost the
+// GEMM +7..10%, 512 MiB +22..27%, 1 GiB +59..69% and one launch per call
+// +100..144%, while the placement gains 3% from 512 MiB on and loses 4%
+// below 256.  An explicit launch size applies to both, unrounded.
 //
 // A launch of 2 workgroups per CU leaves room beside them (VGPRs, waves,
 // LDS) for a workgroup of a concurrent kernel, e.g. the single-wave GEMM's
