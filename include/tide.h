@@ -428,7 +428,10 @@ tide_status tide_pipeline_destroy(tide_pipeline_t pipeline);
  * TIDE_SCRATCH_BYTES (TIDE_ENOSPACE otherwise; 4096 tiles of the default
  * 2048 elements fit); other checks as for tide_rs_tiles_to_stage.  Nothing
  * in the array needs clearing between calls (phase 1 writes every word that
- * phase 2 reads).  Calls and the library allocate nothing.  All calls on one
+ * phase 2 reads).  `stream` must belong to the calling thread's current
+ * device (the null stream does), whose copy of the array the kernels use:
+ * TIDE_EINVAL for a stream of another device.  Calls and the library
+ * allocate nothing.  All calls on one
  * device share its array: calls issued one after another on one stream are
  * ordered, calls that overlap in time on one device (other streams or host
  * threads) race and give undefined results. */

@@ -916,9 +916,17 @@ constexpr int kScratchDevices = 64;
 std::mutex g_scratch_mu;
 float* g_scratch[kScratchDevices];  // device address of `scratch`, per device
 
-tide_status scratch_of_current_device(float** out) {
+// The array's address for the calling thread's current device, which must
+// be the device `stream` belongs to (kernels get that device's address).
+tide_status scratch_for_stream(tide_stream_t stream, float** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TIDE_EHIP;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+            return TIDE_EHIP;
+        if (sdev != dev) return TIDE_EINVAL;
+    }
     if (dev < 0 || dev >= kScratchDevices) return TIDE_EUNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch[dev]) {
@@ -949,7 +957,7 @@ extern "C" tide_status tide_rs_two_phase_noalloc(const void* h_plan, const void*
     if (reinterpret_cast<uintptr_t>(d_plan) % 16) return TIDE_EALIGN;
     if (tile_count == 0) return TIDE_OK;
     float* stage = nullptr;
-    tide_status st = scratch_of_current_device(&stage);
+    tide_status st = scratch_for_stream(stream, &stage);
     if (st != TIDE_OK) return st;
     st = check_pipeline(h_plan, d_plan, tile_begin, tile_count, stage, cap, max_workgroups, &h);
     if (st != TIDE_OK) return st;
