@@ -257,6 +257,7 @@ def pipeline_leg(st, fused_ms: float) -> dict:
     torch.cuda.empty_cache()
     runs = []
     same = True
+    pq = pipeline.Prequeued()
     for phase2 in ("cu", "sdma", "cu64", "cu8"):
         for mult, depth in ((0.25, 2), (1, 1), (1, 2), (1, 4), (4, 2)):
             chunk = max(1, int(L * mult))
@@ -268,6 +269,7 @@ def pipeline_leg(st, fused_ms: float) -> dict:
                 tp.run()
                 host_ms = (time.perf_counter() - h0) * 1e3
                 torch.cuda.synchronize()
+                cmp = pq.compare(tp.run)
             finally:
                 tp.close()
             same = same and all(torch.equal(o[: st.S].view(torch.int32), r.view(torch.int32))
@@ -276,9 +278,14 @@ def pipeline_leg(st, fused_ms: float) -> dict:
             runs.append({"phase2": phase2, "chunk_tiles": chunk, "depth": depth,
                          "staging_mib": round(tp.staging_bytes / 2 ** 20, 1), "ms": round(t, 3),
                          "host_issue_ms": round(host_ms, 3),
-                         # the host needs about as long to issue the chunks
-                         # as the device to run them: the run is host-bound
-                         "host_bound": bool(host_ms >= 0.9 * t),
+                         # on a stream of its own: the call as usual and
+                         # queued before the device starts; slower than its
+                         # pre-queued self, it waits for the host's issue
+                         "own_stream_ms": round(cmp["plain_ms"], 3),
+                         "own_stream_prequeued_ms": (None if cmp["prequeued_ms"] is None
+                                                     else round(cmp["prequeued_ms"], 3)),
+                         "host_bound": (None if cmp["prequeued_ms"] is None
+                                        else bool(cmp["plain_ms"] > 1.1 * cmp["prequeued_ms"])),
                          "overlap": round((serial - t) / min(t1, t2[phase2]), 3)})
             del tp
     del ref

@@ -76,11 +76,66 @@ class TwoPhase:
         self.close()
 
 
+class Prequeued:
+    """Tells a host-bound call from a device-bound one: the call timed as
+    usual and with all of its work queued before the device starts on it,
+    a spin kernel (a bounded count, torch.cuda._sleep) holding the stream
+    while the host issues the call.  A call slower than its pre-queued self
+    waits for the host; the host's issue time alone cannot tell, since a
+    host blocked on a full queue also issues as slowly as the device runs.
+    Both timings run on a stream of this object's own: behind a spin on the
+    null stream, which synchronises with every blocking stream, the
+    pre-queued call measured 10-70% slower than it runs."""
+
+    def __init__(self):
+        import time
+
+        self._time = time.perf_counter
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(10 ** 6)
+            e0.record()
+            torch.cuda._sleep(10 ** 7)
+            e1.record()
+        torch.cuda.synchronize()
+        self.units_per_ms = 1e7 / e0.elapsed_time(e1)
+
+    def compare(self, fn):
+        """{plain_ms, host_issue_ms, prequeued_ms} of fn (which issues its
+        work on the current stream); prequeued_ms is None when the host took
+        most of the spin (2 * issue time + 10 ms) to issue the call, so that
+        the device may have started before the host finished."""
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            h0 = self._time()
+            fn()
+            host = (self._time() - h0) * 1e3
+            a1.record()
+            torch.cuda.synchronize()
+            gate = 2.0 * host + 10.0
+            torch.cuda._sleep(int(gate * self.units_per_ms))
+            b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b0.record()
+            h0 = self._time()
+            fn()
+            issued = (self._time() - h0) * 1e3
+            b1.record()
+            torch.cuda.synchronize()
+        pre = None if issued > 0.8 * gate else b0.elapsed_time(b1)
+        return {"plain_ms": a0.elapsed_time(a1), "host_issue_ms": host, "prequeued_ms": pre}
+
+
 def main(argv=None) -> int:
     """Standalone pipelined runs on one layer, one phase-2 engine and a few
     chunk sizes, for kernel traces: prints one JSON line per configuration
     with the event time of a pipelined call (best of --reps), the host time
-    to issue it, and its bits against the in-place reduce-scatter."""
+    to issue it, the call on a stream of its own timed as usual and queued
+    before the device starts (see Prequeued), and its bits against the
+    in-place reduce-scatter."""
     import argparse
     import json
     import time
@@ -103,6 +158,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ref = [o.view(torch.int32).clone() for o in st.out]
     L = int(st.plan.info.rs_launch_tiles) or int(st.plan.info.rs_tiles)
+    pq = Prequeued()
     for mult in (float(x) for x in a.chunk_launches.split(",")):
         chunk = max(1, int(L * mult))
         with TwoPhase(st.plan, chunk, a.depth, a.phase2, a.phase2_cus) as tp:
@@ -120,10 +176,16 @@ def main(argv=None) -> int:
                 ms = e0.elapsed_time(e1)
                 if best is None or ms < best:
                     best, host = ms, (h1 - h0) * 1e3
+            cmp = pq.compare(tp.run)
         same = all(torch.equal(r, o.view(torch.int32)) for r, o in zip(ref, st.out))
+        pre = cmp["prequeued_ms"]
         print(json.dumps({"workload": w.name, "phase2": a.phase2, "phase2_cus": a.phase2_cus,
                           "chunk_tiles": chunk, "depth": a.depth, "ms": round(best, 3),
-                          "host_issue_ms": round(host, 3), "same_bits": same}), flush=True)
+                          "host_issue_ms": round(host, 3),
+                          "own_stream_ms": round(cmp["plain_ms"], 3),
+                          "own_stream_prequeued_ms": None if pre is None else round(pre, 3),
+                          "host_bound": None if pre is None else bool(cmp["plain_ms"] > 1.1 * pre),
+                          "same_bits": same}), flush=True)
     return 0
 
 

@@ -170,3 +170,23 @@ def test_run_validates_before_issuing():
     finally:
         api.tide_pipeline_destroy(h)
         api.tide_pipeline_destroy(h8)
+
+
+def test_prequeued_timing_of_a_pipelined_call():
+    """The host-bound check behind the pipeline measurements: the same
+    pipelined call timed as usual and queued behind a bounded spin kernel,
+    on a stream of the checker's own; both give finite times of the same
+    order, and the call's results are still the oracle's."""
+    w = _wl([(4096, 96), (1001, 24), (5,)], 8, 951, sigma=1e-3)
+    st = harness.setup(w, with_ag=False)
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    pq = pipeline.Prequeued()
+    assert pq.units_per_ms > 0
+    gu.say("prequeued timing")
+    with pipeline.TwoPhase(st.plan, 16, 2, "cu", 0) as tp:
+        r = pq.compare(tp.run)
+    assert r["plain_ms"] > 0 and r["host_issue_ms"] > 0
+    assert r["prequeued_ms"] is not None
+    assert 0.25 * r["plain_ms"] <= r["prequeued_ms"] <= 4.0 * r["plain_ms"] + 1.0, r
+    gu.check_rs_full(st)
