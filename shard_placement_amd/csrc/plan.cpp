@@ -63,9 +63,11 @@ constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 // A launch of 2 workgroups per CU leaves room beside them (VGPRs, waves,
 // LDS) for a workgroup of a concurrent kernel, e.g. the single-wave GEMM's
 // (256 VGPRs per wave, 65 KB of LDS), which then shares the CU with
-// streaming reduce-scatter waves and finishes late.  (With 8 workgroups per
-// CU, as at R = 8, the wave slots are full and the GEMM waits for the
-// launch boundary instead.)  Such launches therefore hold 64 KB of LDS per
+// streaming reduce-scatter waves and finishes late.  (Launches of many
+// tiles per CU, as at R = 8, keep 5-6 workgroups of 56 VGPRs resident on
+// every CU for their whole length, per the per-tile trace, which leaves no
+// room for the GEMM's 256-VGPR waves; it waits about half a launch.)  Such
+// launches therefore hold 64 KB of LDS per
 // workgroup (the kernel uses 8 KB): two fill 128 of the CU's 160 KB, and a
 // workgroup needing more than 32 KB cannot start beside them.  Measured at
 // R = 64 (512 tiles per launch, two boxes, 4 processes each): GEMM slowdown
