@@ -651,21 +651,48 @@ def main():
 
     sdma = None
     if not args.no_sdma:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.plan.ag_sdma()
+        # the runtime's copy calls beside the kernel placement, each checked
+        # against the kernel's result from the same gathered buffer
+        st.plan.ag()
         torch.cuda.synchronize()
-        reps = 5
+        ref_full = [f.view(torch.int16).clone() for f in st.full]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            st.plan.ag_sdma()
+        for _ in range(5):
+            st.plan.ag()
         e1.record()
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / reps
-        sdma = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
-                "copies": "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run",
-                "engine": "chosen by the HIP runtime (DMA engines or blit kernels; not checked in "
-                          "this run: ag_dma is the path that never uses a compute unit)"}
-        log("AG on copy engines: %.3f ms = %.0f GB/s" % (t, sdma["GB/s"]))
+        t_kernel = e0.elapsed_time(e1) / 5
+        sdma = {}
+        forms = (
+            ("copies_1d", True, "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run",
+             "chosen by the HIP runtime (DMA engines or blit kernels; not checked in this run: "
+             "ag_dma is the path that never uses a compute unit)"),
+            ("copies_2d", False, "hipMemcpy2DAsync per param over the ranks with full shards, "
+             "plus a 1-D copy for the partial rank",
+             "the HIP runtime's blit kernels for 2-D copies (compute units)"),
+        )
+        for key, engine_only, copies, engine in forms:
+            for f in st.full:
+                f.view(torch.int16).fill_(-1)
+            st.plan.ag_sdma(engine_only=engine_only)
+            torch.cuda.synchronize()
+            same = all(torch.equal(f.view(torch.int16), r) for f, r in zip(st.full, ref_full))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                st.plan.ag_sdma(engine_only=engine_only)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 5
+            sdma[key] = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
+                         "vs_kernel": round(t_kernel / t, 3), "same_bits": bool(same),
+                         "copies": copies, "engine": engine}
+            log("AG via %s: %.3f ms = %.0f GB/s (kernel %.3f ms), same bits %s" % (
+                key, t, sdma[key]["GB/s"], t_kernel, same))
+        sdma["kernel_ms"] = round(t_kernel, 4)
+        del ref_full
+        torch.cuda.empty_cache()
 
     # which compute units the reduce-scatter ran on, and for how long (one
     # traced call outside the timed region: same launches, each tile records
