@@ -258,17 +258,21 @@ def pipeline_leg(st, fused_ms: float) -> dict:
     runs = []
     same = True
     pq = pipeline.Prequeued()
+    side = torch.cuda.Stream()
     for phase2 in ("cu", "sdma", "cu64", "cu8"):
         for mult, depth in ((0.25, 2), (1, 1), (1, 2), (1, 4), (4, 2)):
             chunk = max(1, int(L * mult))
             tp = pipeline.TwoPhase(plan, chunk, depth, "sdma" if phase2 == "sdma" else "cu",
                                    link.get(phase2, 0))
             try:
-                t = ev_time(tp.run, reps=2 if phase2 == "cu" else 1)
-                h0 = time.perf_counter()
-                tp.run()
-                host_ms = (time.perf_counter() - h0) * 1e3
-                torch.cuda.synchronize()
+                # back to back on a stream of their own: on the null stream the
+                # pipeline's blocking CU-masked streams wait on its pending work
+                with torch.cuda.stream(side):
+                    t = ev_time(tp.run, reps=2 if phase2 == "cu" else 1)
+                    h0 = time.perf_counter()
+                    tp.run()
+                    host_ms = (time.perf_counter() - h0) * 1e3
+                    torch.cuda.synchronize()
                 cmp = pq.compare(tp.run)
             finally:
                 tp.close()

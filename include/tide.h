@@ -407,7 +407,11 @@ tide_status tide_stream_destroy(tide_stream_t stream);
  * before its later work; asynchronous.  All checks are made before anything
  * is issued.  Calls on one object must not overlap in time from several
  * host threads; calls issued one after another on the same stream may
- * share the ring. */
+ * share the ring.  The object's streams are CU-masked, which HIP creates as
+ * blocking streams: calls issued back to back on the null stream, whose
+ * pending work every blocking stream then waits on implicitly, measured up
+ * to 20% slower than on another stream (or with the host waiting between
+ * calls), so issue them from a stream other than the null stream. */
 typedef struct tide_pipeline *tide_pipeline_t;
 tide_status tide_pipeline_create(int32_t depth, int32_t phase2_cus, tide_pipeline_t *out);
 tide_status tide_pipeline_run(tide_pipeline_t pipeline, const void *h_plan, const void *d_plan,

@@ -56,7 +56,10 @@ class TwoPhase:
 
     def run(self) -> None:
         """The whole reduce-scatter through the pipeline, ordered after the
-        current stream's earlier work and before its later work."""
+        current stream's earlier work and before its later work.  Issue
+        back-to-back calls from a stream other than the null stream (torch's
+        default): the pipeline's CU-masked streams are blocking streams, and
+        with work pending on the null stream they measured up to 20% slower."""
         if self.handle is None:
             raise RuntimeError("pipeline closed")
         api.tide_pipeline_run(self.handle, self.plan.blob, self.plan.d_blob, self.chunk,
