@@ -13,7 +13,7 @@ the tiny one on the CPU.
 """
 from __future__ import annotations
 
-from typing import List, Sequence, Tuple
+from typing import List, Sequence
 
 import torch
 
@@ -56,21 +56,6 @@ def fill_normal_(buf: torch.Tensor, seed: int, sigma: float) -> torch.Tensor:
             tmp.mul_(sigma)
         flat[start:stop].copy_(tmp)  # float32 -> bf16, round to nearest even
     return buf
-
-
-def rank_grads(shapes, R: int, key: int, sigma: float, device,
-               same_for_all: bool = False) -> Tuple[List[torch.Tensor], List[List[torch.Tensor]]]:
-    """Return (arenas, grads): arenas[q] is rank q's flat bf16 arena and
-    grads[q][p] its per-parameter views.  ``same_for_all`` makes every rank
-    a copy of rank 0 (seed of rank 0)."""
-    n = arena_numel(shapes)
-    arenas, grads = [], []
-    for q in range(R):
-        a = torch.empty(n, dtype=torch.bfloat16, device=device)
-        fill_normal_(a, SEED_STRIDE * key + (0 if same_for_all else q), sigma)
-        arenas.append(a)
-        grads.append(views(a, shapes))
-    return arenas, grads
 
 
 def integer_grid_(buf: torch.Tensor, seed: int, kmax: int = 127, scale_log2: int = -10) -> torch.Tensor:
