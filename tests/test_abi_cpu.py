@@ -615,3 +615,24 @@ def test_streams_variant_validates_before_touching_the_gpu():
     assert F(np.zeros(4096, np.uint8).ctypes.data, fake_dev, 0, 0, two, 2) == -7
     ag_blob, _ = api.tide_desc_build(SHAPES, R, None, None, ga, f)
     assert F(ag_blob.ctypes.data, fake_dev, 0, 0, two, 2) == -6
+
+
+def test_bench_refuses_several_gpus_and_needs_one():
+    """bench.py measures one GPU: --gpus above 1 exits with a message that
+    says so, and without a visible GPU it fails instead of falling back to
+    anything on the host."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+    import torch
+
+    if not torch.cuda.is_available():
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "1",
+                            "--warmup", "0"], capture_output=True, text=True, timeout=300)
+        assert r.returncode != 0
+        assert "no GPU" in r.stderr
+        assert not r.stdout.strip().startswith("{")
