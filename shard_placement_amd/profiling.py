@@ -40,18 +40,23 @@ def kernel_trace(d: str):
         return list(csv.DictReader(fh))
 
 
-def idle_stretches(trace, n: int = 3):
+def idle_stretches(trace, n: int = 3, names: bool = False):
     """The n longest stretches of a kernel trace with no dispatch running
     (between the end of the last dispatch so far and the start of the
-    next), as (length, start, end) in ms from the first dispatch."""
-    iv = sorted((int(t["Start_Timestamp"]), int(t["End_Timestamp"])) for t in trace)
+    next), as (length, start, end) in ms from the first dispatch; with
+    names=True each also carries the kernel that ended last before the
+    stretch and the one that starts it."""
+    iv = sorted((int(t["Start_Timestamp"]), int(t["End_Timestamp"]), t.get("Kernel_Name", ""))
+                for t in trace)
     if not iv:
         return []
-    t0, reach, gaps = iv[0][0], iv[0][1], []
-    for a, b in iv[1:]:
+    t0, reach, last, gaps = iv[0][0], iv[0][1], iv[0][2], []
+    for a, b, k in iv[1:]:
         if a > reach:
-            gaps.append(((a - reach) / 1e6, (reach - t0) / 1e6, (a - t0) / 1e6))
-        reach = max(reach, b)
+            g = ((a - reach) / 1e6, (reach - t0) / 1e6, (a - t0) / 1e6)
+            gaps.append(g + (last, k) if names else g)
+        if b >= reach:
+            reach, last = b, k
     return sorted(gaps, reverse=True)[:n]
 
 
@@ -84,8 +89,9 @@ def summarize_stats(d: str, out: str, command: str, top: int = 12, gaps: int = 0
         if gaps:
             lines.append("")
             lines.append("# the longest stretches with no kernel dispatch running (ms from the first dispatch)")
-            for g, a, b in idle_stretches(tr, gaps):
-                lines.append("no dispatch for %.1f ms: %.3f .. %.3f ms" % (g, a, b))
+            for g, a, b, before, after in idle_stretches(tr, gaps, names=True):
+                lines.append("no dispatch for %.1f ms: %.3f .. %.3f ms (after %s; before %s)" % (
+                    g, a, b, before[:60], after[:60]))
     except FileNotFoundError:
         pass
     with open(out, "w") as fh:

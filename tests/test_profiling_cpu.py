@@ -99,3 +99,9 @@ def test_idle_stretches():
           for a, b in [(0, 10), (5, 12), (40, 50), (50, 51), (200, 210), (60, 70)]]
     assert idle_stretches(tr, 2) == [(130.0, 70.0, 200.0), (28.0, 12.0, 40.0)]
     assert idle_stretches([], 3) == []
+    for i, t in enumerate(tr):
+        t["Kernel_Name"] = "k%d" % i
+    # the stretch 70..200 follows k5 (ends at 70) and precedes k4; 12..40
+    # follows k1 (the later end of the overlapping pair) and precedes k2
+    assert idle_stretches(tr, 2, names=True) == [(130.0, 70.0, 200.0, "k5", "k4"),
+                                                 (28.0, 12.0, 40.0, "k1", "k2")]
