@@ -43,13 +43,16 @@
  *     round-to-nearest-even add, subnormals kept.
  *
  * Memory and ownership: the caller owns every buffer, including the plan
- * blob (host) and its device copy.  The library allocates no device memory.
+ * blob (host) and its device copy.  The library allocates no device memory
+ * (its one device array, the staging array of tide_rs_two_phase_noalloc, is
+ * part of its code object).
  * Kernel launches are asynchronous on the caller's stream and synchronise
  * nothing; the copy-engine calls issued through ROCr (tide_ag_place_dma,
  * tide_rs_stage_dma) are host-synchronous instead (they wait for the
  * caller's stream, then for their copies).  The only state kept between
  * calls is, per device, the ROCr agent and copy-engine list those calls look
- * up once (guarded by a mutex).  Streams and pipeline objects the library
+ * up once and the staging array's device address (each guarded by a
+ * mutex).  Streams and pipeline objects the library
  * creates on request are the caller's to release.  A plan holds raw device addresses: it is
  * invalid once any of them is freed.
  *
@@ -215,7 +218,7 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
  * Measured on MI355X with two queues: 6.46-6.54 TB/s against 5.99 on the
  * R = 64 layer, 5.92-6.08 against 5.58 on the R = 16 MoE layer, none on the
  * R = 8 layer; but a concurrent single-wave GEMM then loses the launch
- * boundaries that let it in (+12..88% against +2..6%): a mode for when no
+ * boundaries that let it in (+12..92% against +1..7%): a mode for when no
  * compute runs beside the reduce-scatter.  The caller orders the streams
  * against its other work (e.g. the others wait for an event of the first,
  * the first waits for events of the others).  n_streams in [1, 64]; with
@@ -355,11 +358,13 @@ tide_status tide_rs_stage_to_shards(const void *h_plan, const void *d_plan, int6
                                     int64_t tile_count, const float *stage, int64_t stage_elems,
                                     int32_t max_workgroups, tide_stream_t stream);
 
-/* Phase 2 on the DMA engines instead of a kernel, with a copy engine's
- * bandwidth (tens of GB/s, about a network link's) standing in for the
- * network: one stream-ordered copy of the no-compute-unit kind per run of
- * tiles contiguous in both the chunk and a rank's arena.  Asynchronous on
- * `stream`; same arguments and checks as tide_rs_stage_to_shards. */
+/* Phase 2 with the runtime's no-compute-unit copy kind instead of a kernel
+ * (a network stand-in that leaves the compute units alone when the runtime
+ * gives the copies to the DMA engines; it may also run them as small blit
+ * kernels, the caveat of tide_ag_place_sdma): one stream-ordered copy per
+ * run of tiles contiguous in both the chunk and a rank's arena (measured
+ * 5.2-5.3 ms for the 3.5 GB of shards of the R = 64 layer).  Asynchronous
+ * on `stream`; same arguments and checks as tide_rs_stage_to_shards. */
 tide_status tide_rs_stage_to_shards_sdma(const void *h_plan, int64_t tile_begin,
                                          int64_t tile_count, const float *stage,
                                          int64_t stage_elems, tide_stream_t stream);
