@@ -502,6 +502,180 @@ def others_leg(keys, args, reps: int = 10) -> dict:
     return out
 
 
+def tree_leg(st, rsb: int) -> float:
+    """The optional pairwise (tree) rank order, same tiles and launches: ms
+    per call.  Leaves the fixed-order shards in place for later checks."""
+    import torch
+
+    st.plan.rs(order="tree")
+    torch.cuda.synchronize()
+    te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    te0.record()
+    for _ in range(3):
+        st.plan.rs(order="tree")
+    te1.record()
+    torch.cuda.synchronize()
+    tree_ms = te0.elapsed_time(te1) / 3
+    st.plan.rs()
+    torch.cuda.synchronize()
+    log("RS tree order: %.3f ms = %.0f GB/s" % (tree_ms, rsb / (tree_ms * 1e-3) / 1e9))
+    return tree_ms
+
+
+def graph_leg(step, steps: int) -> float:
+    """The step captured once in a HIP graph and replayed (launch-bound host
+    work removed; the device work is identical): ms per step."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ge0.record()
+    for _ in range(steps):
+        g.replay()
+    ge1.record()
+    torch.cuda.synchronize()
+    graph_ms = ge0.elapsed_time(ge1) / steps
+    log("step as a HIP graph: %.3f ms" % graph_ms)
+    return graph_ms
+
+
+def sdma_leg(st, agb: int) -> dict:
+    """The runtime's copy calls beside the kernel placement (1-D copies of
+    the no-compute-unit kind, and 2-D copies), each checked against the
+    kernel's result from the same gathered buffer."""
+    import torch
+
+    st.plan.ag()
+    torch.cuda.synchronize()
+    ref_full = [f.view(torch.int16).clone() for f in st.full]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        st.plan.ag()
+    e1.record()
+    torch.cuda.synchronize()
+    t_kernel = e0.elapsed_time(e1) / 5
+    sdma = {}
+    forms = (
+        ("copies_1d", True, "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run",
+         "chosen by the HIP runtime (DMA engines or blit kernels; not checked in this run: "
+         "ag_dma is the path that never uses a compute unit)"),
+        ("copies_2d", False, "hipMemcpy2DAsync per param over the ranks with full shards, "
+         "plus a 1-D copy for the partial rank",
+         "the HIP runtime's blit kernels for 2-D copies (compute units)"),
+    )
+    for key, engine_only, copies, engine in forms:
+        for f in st.full:
+            f.view(torch.int16).fill_(-1)
+        st.plan.ag_sdma(engine_only=engine_only)
+        torch.cuda.synchronize()
+        same = all(torch.equal(f.view(torch.int16), r) for f, r in zip(st.full, ref_full))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            st.plan.ag_sdma(engine_only=engine_only)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 5
+        sdma[key] = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
+                     "vs_kernel": round(t_kernel / t, 3), "same_bits": bool(same),
+                     "copies": copies, "engine": engine}
+        log("AG via %s: %.3f ms = %.0f GB/s (kernel %.3f ms), same bits %s" % (
+            key, t, sdma[key]["GB/s"], t_kernel, same))
+    sdma["kernel_ms"] = round(t_kernel, 4)
+    del ref_full
+    torch.cuda.empty_cache()
+    return sdma
+
+
+def trace_leg(st, max_wg: int):
+    """Which compute units the reduce-scatter ran on, and for how long: one
+    traced call outside the timed region (same launches; each tile records
+    its CU's hardware id and its start and end on the real-time counter).
+    Returns (CU-time record, distinct CUs, CUs per XCC)."""
+    import torch
+
+    from shard_placement_amd import profiling
+
+    st.plan.rs_trace(max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    te0.record()
+    census, stamps = st.plan.rs_trace(max_workgroups=max_wg)
+    te1.record()
+    torch.cuda.synchronize()
+    ids = census.cpu().numpy()
+    cu_rec = profiling.cu_time(ids, stamps.cpu().numpy())
+    cu_rec["traced_call_ms_events"] = round(te0.elapsed_time(te1), 4)
+    per_xcc = {}
+    for v in set(ids.tolist()):
+        per_xcc[v >> 8] = per_xcc.get(v >> 8, 0) + 1
+    log("census: %d distinct CUs over %d tiles; per XCC %s; CU time %s" % (
+        cu_rec["cus"], len(ids), dict(sorted(per_xcc.items())), cu_rec))
+    st.plan.rs()  # the untraced result for the checks that follow
+    torch.cuda.synchronize()
+    return cu_rec, cu_rec["cus"], per_xcc
+
+
+def probe_leg(st, args, rsb: int) -> dict:
+    """The single-wave GEMM beside the reduce-scatter in the default
+    configuration; with --probe also launch sizes, a capped grid and CU
+    masks."""
+    from shard_placement_amd import api, probe
+
+    w = st.w
+
+    def plan_with(mib):
+        return api.Plan(w.shapes, w.R, grads=st.grads, out=st.out, flags=args.flags,
+                        rs_tile=args.rs_tile, launch_mib=mib)
+
+    info = st.plan.info
+    modes = [("default (%d MiB launches)" % (info.rs_launch_tiles * info.rs_tile_elems *
+                                              (2 * w.R + 4) >> 20), st.plan, 0, 0)]
+    if args.probe:
+        one = plan_with(-1)
+        modes += [("256 MiB launches", plan_with(256), 0, 0),
+                  ("128 MiB launches", plan_with(128), 0, 0),
+                  ("64 MiB launches", plan_with(64), 0, 0),
+                  ("one launch", one, 0, 0),
+                  ("one launch, grid 256", one, 256, 0),
+                  ("one launch, CU mask 32", one, 0, 32)]
+        # the default launches confined to part of the chip
+        modes += [("default launches, CU mask %d" % n, st.plan, 0, n) for n in (128, 64, 32, 16)]
+    res = probe.run(modes, rsb, iters=40)
+    for m in res["modes"]:
+        log("probe", m)
+    return res
+
+
+def pages_context(rec: dict, cu_rec: dict, stock_rec) -> dict:
+    """The pages' figures (other hardware) beside this GPU's analogs."""
+    import torch
+
+    ctx = dict(PAGES_CONTEXT)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    ctx["one_gpu_analogs"] = {
+        "gemm_slowdown_pct": rec["gemm_slowdown_pct"],
+        "rs_cu_ms_fused": cu_rec["held_cu_ms"],
+        # the analog's torch kernels have grids of far more than one
+        # workgroup per CU: all CUs for its whole duration
+        "rs_cu_ms_stock_analog": round(n_cu * stock_rec["rs_ms"], 1) if stock_rec else None,
+        "rs_cu_time_stock_over_fused": (round(n_cu * stock_rec["rs_ms"] / cu_rec["held_cu_ms"], 2)
+                                        if stock_rec and cu_rec.get("held_cu_ms") else None),
+        "stock_analog_pack_pct_of_its_rs": (round(100 * stock_rec["pack_ms"] / stock_rec["rs_ms"], 1)
+                                            if stock_rec else None),
+        "fused_rs_speedup_over_stock_analog": stock_rec["fused_rs_speedup"] if stock_rec else None,
+    }
+    return ctx
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -548,7 +722,7 @@ def main():
 
     import torch
 
-    from shard_placement_amd import configs, harness, profiling
+    from shard_placement_amd import configs, harness
 
     if not torch.cuda.is_available():
         print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
@@ -617,110 +791,15 @@ def main():
     log("step %.3f ms; RS avg %.3f ms (min %.3f) = %.0f GB/s; AG avg %.3f ms = %.0f GB/s" % (
         ms_step, rs_avg, min(rs_ms), rs_gbs, ag_avg, ag_gbs))
 
-    # the optional pairwise (tree) rank order, same tiles and launches
-    st.plan.rs(order="tree")
-    torch.cuda.synchronize()
-    te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    te0.record()
-    for _ in range(3):
-        st.plan.rs(order="tree")
-    te1.record()
-    torch.cuda.synchronize()
-    tree_ms = te0.elapsed_time(te1) / 3
-    st.plan.rs()  # leave the fixed-order shards in place for the checks below
-    torch.cuda.synchronize()
-    log("RS tree order: %.3f ms = %.0f GB/s" % (tree_ms, rsb / (tree_ms * 1e-3) / 1e9))
+    tree_ms = tree_leg(st, rsb)
 
-    # the same step captured once in a HIP graph and replayed (launch-bound
-    # host work removed; the device work is identical)
-    graph_ms = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            step()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ge0.record()
-        for _ in range(args.steps):
-            g.replay()
-        ge1.record()
-        torch.cuda.synchronize()
-        graph_ms = ge0.elapsed_time(ge1) / args.steps
-        log("step as a HIP graph: %.3f ms" % graph_ms)
-        del g
+    graph_ms = None if args.no_graph else graph_leg(step, args.steps)
 
-    sdma = None
-    if not args.no_sdma:
-        # the runtime's copy calls beside the kernel placement, each checked
-        # against the kernel's result from the same gathered buffer
-        st.plan.ag()
-        torch.cuda.synchronize()
-        ref_full = [f.view(torch.int16).clone() for f in st.full]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            st.plan.ag()
-        e1.record()
-        torch.cuda.synchronize()
-        t_kernel = e0.elapsed_time(e1) / 5
-        sdma = {}
-        forms = (
-            ("copies_1d", True, "hipMemcpyDeviceToDeviceNoCU 1-D copies, one per (param, rank) run",
-             "chosen by the HIP runtime (DMA engines or blit kernels; not checked in this run: "
-             "ag_dma is the path that never uses a compute unit)"),
-            ("copies_2d", False, "hipMemcpy2DAsync per param over the ranks with full shards, "
-             "plus a 1-D copy for the partial rank",
-             "the HIP runtime's blit kernels for 2-D copies (compute units)"),
-        )
-        for key, engine_only, copies, engine in forms:
-            for f in st.full:
-                f.view(torch.int16).fill_(-1)
-            st.plan.ag_sdma(engine_only=engine_only)
-            torch.cuda.synchronize()
-            same = all(torch.equal(f.view(torch.int16), r) for f, r in zip(st.full, ref_full))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(5):
-                st.plan.ag_sdma(engine_only=engine_only)
-            e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) / 5
-            sdma[key] = {"ms": round(t, 4), "GB/s": round(agb / (t * 1e-3) / 1e9, 1),
-                         "vs_kernel": round(t_kernel / t, 3), "same_bits": bool(same),
-                         "copies": copies, "engine": engine}
-            log("AG via %s: %.3f ms = %.0f GB/s (kernel %.3f ms), same bits %s" % (
-                key, t, sdma[key]["GB/s"], t_kernel, same))
-        sdma["kernel_ms"] = round(t_kernel, 4)
-        del ref_full
-        torch.cuda.empty_cache()
+    sdma = None if args.no_sdma else sdma_leg(st, agb)
 
-    # which compute units the reduce-scatter ran on, and for how long (one
-    # traced call outside the timed region: same launches, each tile records
-    # its CU's hardware id and its start and end on the real-time counter)
     cu_rec, cus_measured, per_xcc = {"held_cu_ms": None}, None, {}
     if not args.no_trace:
-        st.plan.rs_trace(max_workgroups=args.max_wg)
-        torch.cuda.synchronize()
-        te0, te1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        te0.record()
-        census, stamps = st.plan.rs_trace(max_workgroups=args.max_wg)
-        te1.record()
-        torch.cuda.synchronize()
-        ids = census.cpu().numpy()
-        cu_rec = profiling.cu_time(ids, stamps.cpu().numpy())
-        cu_rec["traced_call_ms_events"] = round(te0.elapsed_time(te1), 4)
-        cus_measured = cu_rec["cus"]
-        for v in set(ids.tolist()):
-            per_xcc[v >> 8] = per_xcc.get(v >> 8, 0) + 1
-        log("census: %d distinct CUs over %d tiles; per XCC %s; CU time %s" % (
-            cus_measured, len(ids), dict(sorted(per_xcc.items())), cu_rec))
-        st.plan.rs()  # the untraced result for the checks below
-        torch.cuda.synchronize()
-        del census, stamps
+        cu_rec, cus_measured, per_xcc = trace_leg(st, args.max_wg)
 
     dma_rec = staged_rec = None
     if not args.no_staged:
@@ -741,33 +820,7 @@ def main():
         stock_rec["fused_ag_speedup"] = round(stock_rec["ag_ms"] / ag_avg, 2)
         log("stock-FSDP2 analog", stock_rec)
 
-    probe = None
-    if not args.no_probe:
-        from shard_placement_amd import probe as probe_mod
-
-        from shard_placement_amd import api as api_mod
-
-        def plan_with(mib):
-            return api_mod.Plan(w.shapes, w.R, grads=st.grads, out=st.out, flags=args.flags,
-                                rs_tile=args.rs_tile, launch_mib=mib)
-
-        modes = [("default (%d MiB launches)" % (st.plan.info.rs_launch_tiles *
-                                                   st.plan.info.rs_tile_elems * (2 * w.R + 4) >> 20),
-                  st.plan, 0, 0)]
-        if args.probe:
-            one = plan_with(-1)
-            modes += [("256 MiB launches", plan_with(256), 0, 0),
-                      ("128 MiB launches", plan_with(128), 0, 0),
-                      ("64 MiB launches", plan_with(64), 0, 0),
-                      ("one launch", one, 0, 0),
-                      ("one launch, grid 256", one, 256, 0),
-                      ("one launch, CU mask 32", one, 0, 32)]
-            # the default launches confined to part of the chip
-            modes += [("default launches, CU mask %d" % n, st.plan, 0, n) for n in (128, 64, 32, 16)]
-        probe = probe_mod.run(modes, rsb, iters=40)
-        for m in probe["modes"]:
-            log("probe", m)
-        del modes
+    probe = None if args.no_probe else probe_leg(st, args, rsb)
 
     two_q = None
     if not args.no_two_queues:
@@ -847,22 +900,7 @@ def main():
         "env": {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
                 "hip": torch.version.hip, "host_threads": len(os.sched_getaffinity(0))},
     }
-    # the pages' figures (other hardware) beside this GPU's analogs of them
-    ctx = dict(PAGES_CONTEXT)
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    ctx["one_gpu_analogs"] = {
-        "gemm_slowdown_pct": rec["gemm_slowdown_pct"],
-        "rs_cu_ms_fused": cu_rec["held_cu_ms"],
-        # the analog's torch kernels have grids of far more than one
-        # workgroup per CU: all CUs for its whole duration
-        "rs_cu_ms_stock_analog": round(n_cu * stock_rec["rs_ms"], 1) if stock_rec else None,
-        "rs_cu_time_stock_over_fused": (round(n_cu * stock_rec["rs_ms"] / cu_rec["held_cu_ms"], 2)
-                                        if stock_rec and cu_rec.get("held_cu_ms") else None),
-        "stock_analog_pack_pct_of_its_rs": (round(100 * stock_rec["pack_ms"] / stock_rec["rs_ms"], 1)
-                                            if stock_rec else None),
-        "fused_rs_speedup_over_stock_analog": stock_rec["fused_rs_speedup"] if stock_rec else None,
-    }
-    rec["pages_context"] = ctx
+    rec["pages_context"] = pages_context(rec, cu_rec, stock_rec)
     keys = [k for k in args.others.split(",") if k.strip() and configs.get(k).key != w.key]
     if keys:
         st.free()
