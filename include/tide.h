@@ -224,7 +224,13 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
  * the first waits for events of the others).  n_streams in [1, 64]; with
  * more than one stream none may be the null stream (TIDE_EINVAL: it
  * synchronises with every blocking stream, which would serialise the
- * launches; measured 72 ms against 19 ms for one stream). */
+ * launches; measured 72 ms against 19 ms for one stream).  HIP backs a
+ * process's streams with a small pool of hardware queues (GPU_MAX_HW_QUEUES,
+ * 4 by default); once that many are in use, a new stream, CU-masked or not,
+ * shares one, and launches dealt over streams on one queue run one after
+ * the other: after three other streams had been created, the two-queue call
+ * fell from 6.52 to 5.92 TB/s, the one-queue rate.  Create these streams
+ * early and keep them. */
 tide_status tide_rs_bf16_to_fp32_streams(const void *h_plan, const void *d_plan,
                                          int32_t order, int32_t max_workgroups,
                                          const tide_stream_t *streams, int32_t n_streams);
@@ -393,7 +399,10 @@ tide_status tide_stream_destroy(tide_stream_t stream);
  * floats, then moved to the shard arenas by phase 2 (phase2 = 0: the
  * tide_rs_stage_to_shards kernel; 1: the copy-kind copies of
  * tide_rs_stage_to_shards_sdma).  The phases run on two streams of the
- * pipeline object, each with a hardware queue of its own, ordered per slot
+ * pipeline object, each with a hardware queue of its own (when the
+ * process's pool of hardware queues still has one free for each, see
+ * tide_rs_bf16_to_fp32_streams; otherwise the phases run one after the
+ * other), ordered per slot
  * by events: phase 2 of chunk i after its phase 1, phase 1 of chunk i after
  * phase 2 of chunk i - depth.  The result is bit-identical to
  * tide_rs_bf16_to_fp32 with order 0.
