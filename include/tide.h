@@ -226,11 +226,14 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
  * synchronises with every blocking stream, which would serialise the
  * launches; measured 72 ms against 19 ms for one stream).  HIP backs a
  * process's streams with a small pool of hardware queues (GPU_MAX_HW_QUEUES,
- * 4 by default); once that many are in use, a new stream, CU-masked or not,
- * shares one, and launches dealt over streams on one queue run one after
- * the other: after three other streams had been created, the two-queue call
- * fell from 6.52 to 5.92 TB/s, the one-queue rate.  Create these streams
- * early and keep them. */
+ * 4 by default), handed out in turn, so streams created far apart can
+ * share one (CU-masked ones too), and launches dealt over streams on one
+ * queue run one after the other.  Measured: two masked streams created one
+ * right after the other kept 6.42-6.54 TB/s whatever the process created
+ * before or after them (five ordinary streams), while one created before
+ * and one after five ordinary streams shared a queue (5.90 TB/s, the
+ * one-queue rate).  So create the streams to deal over one right after the
+ * other. */
 tide_status tide_rs_bf16_to_fp32_streams(const void *h_plan, const void *d_plan,
                                          int32_t order, int32_t max_workgroups,
                                          const tide_stream_t *streams, int32_t n_streams);
@@ -399,10 +402,9 @@ tide_status tide_stream_destroy(tide_stream_t stream);
  * floats, then moved to the shard arenas by phase 2 (phase2 = 0: the
  * tide_rs_stage_to_shards kernel; 1: the copy-kind copies of
  * tide_rs_stage_to_shards_sdma).  The phases run on two streams of the
- * pipeline object, each with a hardware queue of its own (when the
- * process's pool of hardware queues still has one free for each, see
- * tide_rs_bf16_to_fp32_streams; otherwise the phases run one after the
- * other), ordered per slot
+ * pipeline object, created one right after the other so that each gets
+ * a hardware queue of its own (see tide_rs_bf16_to_fp32_streams), ordered
+ * per slot
  * by events: phase 2 of chunk i after its phase 1, phase 1 of chunk i after
  * phase 2 of chunk i - depth.  The result is bit-identical to
  * tide_rs_bf16_to_fp32 with order 0.
