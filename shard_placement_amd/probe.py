@@ -137,20 +137,30 @@ def _run(modes, rs_bytes, iters, M, N, K) -> Dict:
             # the GEMM train is queued right after the first reduce-scatter
             # call, so that its queue holds work while the reduce-scatter
             # runs however long the host takes to issue the rest
-            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            r0.record(rs_stream)
-            plan.rs(max_workgroups=max_wg, stream=rs_stream)
-            gemm_stream.wait_event(r0)
-            conc = _gemm_train(a, b, c, gemm_stream, iters)
-            for _ in range(n_rs - 1):
+            # an event before and after every call marks the calls' own spans
+            calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(n_rs)]
+            r0 = calls[0][0]
+            for k, (c0, c1) in enumerate(calls):
+                c0.record(rs_stream)
                 plan.rs(max_workgroups=max_wg, stream=rs_stream)
-            r1.record(rs_stream)
+                c1.record(rs_stream)
+                if k == 0:
+                    gemm_stream.wait_event(r0)
+                    conc = _gemm_train(a, b, c, gemm_stream, iters)
             torch.cuda.synchronize()
-            window = r0.elapsed_time(r1)
+            window = r0.elapsed_time(calls[-1][1])
             inside = [e1.elapsed_time(e2) for e1, e2 in conc
                       if r0.elapsed_time(e1) >= 0.0 and r0.elapsed_time(e2) <= window]
             t1 = _median(inside)
             rs_conc = window / n_rs
+            # did the two trains run side by side?  Streams that share a
+            # hardware queue run one after the other: then every GEMM falls
+            # between the end of one call and the start of the next
+            spans = [(r0.elapsed_time(c0), r0.elapsed_time(c1)) for c0, c1 in calls]
+            gemms = [(r0.elapsed_time(e1), r0.elapsed_time(e2)) for e1, e2 in conc]
+            overlapping = sum(1 for g0, g1 in gemms
+                              if any(min(g1, s1) - max(g0, s0) > 0.1 * (g1 - g0) for s0, s1 in spans))
             info = plan.info
             out["modes"].append({
                 "mode": name, "max_workgroups": max_wg or None, "cu_mask": n_cu or None,
@@ -163,6 +173,8 @@ def _run(modes, rs_bytes, iters, M, N, K) -> Dict:
                 "t_gemm_alone_ms": round(t0m, 4),
                 "t_gemm_concurrent_ms": round(t1, 4) if t1 else None,
                 "gemm_inside": len(inside),
+                "gemms_overlapping_rs": overlapping,
+                "ran_concurrently": bool(overlapping > 0),
                 # no GEMM inside the window: it waited for the whole train
                 "gemm_slowdown_pct": round(100.0 * (t1 / t0m - 1.0), 2) if t1 else "starved",
             })

@@ -133,6 +133,9 @@ def test_probe_smoke():
     m = res["modes"][0]
     assert res["t_gemm_alone_ms"] > 0 and m["t_gemm_alone_ms"] > 0
     assert m["gemm_inside"] >= 1
+    # the GEMM train and the reduce-scatter calls overlapped in time (on
+    # streams of different hardware queues), so the slowdown is measured
+    assert m["ran_concurrently"], m
     assert isinstance(m["gemm_slowdown_pct"], float) and np.isfinite(m["gemm_slowdown_pct"])
     assert m["rs_alone_gbps"] > 0 and m["rs_concurrent_gbps"] > 0
     assert m["launches_per_rs"] == -(-int(st.plan.info.rs_tiles) // int(st.plan.info.rs_launch_tiles))
@@ -180,3 +183,23 @@ def test_trace_same_bits_and_sane_stamps():
         assert 1 <= len(set(c8.cpu().tolist())) <= 8
     finally:
         api.tide_stream_destroy(sm)
+
+
+def test_probe_flags_serialised_streams(monkeypatch):
+    """The probe's overlap check: with the reduce-scatter and the GEMM train
+    on one stream (what two streams on one hardware queue amount to) no GEMM
+    overlaps a reduce-scatter call, and the probe says so instead of
+    reporting a slowdown that was never measured beside the reduce-scatter."""
+    w = _wl(406)
+    st = harness.setup(w, with_ag=False, guard=0)
+    one = torch.cuda.Stream()
+    monkeypatch.setattr(probe.torch.cuda, "Stream", lambda *a, **k: one)
+    monkeypatch.setattr(probe.api, "tide_stream_create_cu_limited", lambda n: one)
+    monkeypatch.setattr(probe.api, "tide_stream_destroy", lambda s: None)
+    gu.say("probe on one stream")
+    res = probe.run([("one stream", st.plan, 0, 0)], harness.rs_bytes(w), iters=12)
+    torch.cuda.synchronize()
+    m = res["modes"][0]
+    assert m["gemms_overlapping_rs"] == 0, m
+    assert not m["ran_concurrently"]
+    gu.check_rs_full(st)
