@@ -73,6 +73,12 @@ class DealtRS:
         self.plan.rs_streams(self.extra, max_workgroups=max_workgroups, stream=stream)
 
 
+def _new_stream():
+    """The stream the GEMM trains run on (its own, so that it gets a
+    hardware queue apart from the reduce-scatter's)."""
+    return torch.cuda.Stream()
+
+
 def _gemm_train(a, b, c, stream, n):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]
@@ -106,7 +112,7 @@ def _run(modes, rs_bytes, iters, M, N, K) -> Dict:
     a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
     b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
     c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-    gemm_stream = torch.cuda.Stream()
+    gemm_stream = _new_stream()
     for _ in range(5):
         torch.matmul(a, b, out=c)
     torch.cuda.synchronize()
@@ -199,7 +205,7 @@ def _gemm_during(host_call, expect_ms, M, N, K) -> Dict:
     a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
     b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
     c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-    s = torch.cuda.Stream()
+    s = _new_stream()
     for _ in range(5):
         torch.matmul(a, b, out=c)
     torch.cuda.synchronize()

@@ -193,9 +193,10 @@ def test_probe_flags_serialised_streams(monkeypatch):
     w = _wl(406)
     st = harness.setup(w, with_ag=False, guard=0)
     one = torch.cuda.Stream()
-    monkeypatch.setattr(probe.torch.cuda, "Stream", lambda *a, **k: one)
+    monkeypatch.setattr(probe, "_new_stream", lambda: one)
     monkeypatch.setattr(probe.api, "tide_stream_create_cu_limited", lambda n: one)
     monkeypatch.setattr(probe.api, "tide_stream_destroy", lambda s: None)
+    before = torch.cuda.current_stream()
     gu.say("probe on one stream")
     res = probe.run([("one stream", st.plan, 0, 0)], harness.rs_bytes(w), iters=12)
     torch.cuda.synchronize()
@@ -203,3 +204,4 @@ def test_probe_flags_serialised_streams(monkeypatch):
     assert m["gemms_overlapping_rs"] == 0, m
     assert not m["ran_concurrently"]
     gu.check_rs_full(st)
+    assert torch.cuda.current_stream() == before
