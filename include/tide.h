@@ -215,7 +215,7 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
  * streams[i % n_streams]), so that with streams on different hardware queues
  * (e.g. from tide_stream_create_cu_limited) a launch can start on the CUs the
  * previous one is vacating instead of waiting for it to drain.  Same results.
- * Measured on MI355X with two queues: 6.46-6.54 TB/s against 5.99 on the
+ * Measured on MI355X with two queues: 6.46-6.57 TB/s against 5.99 on the
  * R = 64 layer, 5.92-6.08 against 5.58 on the R = 16 MoE layer, none on the
  * R = 8 layer; but a concurrent single-wave GEMM then loses the launch
  * boundaries that let it in (+12..92% against +1..7%): a mode for when no
