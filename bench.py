@@ -448,9 +448,13 @@ def two_queue_leg(st, rsb: int, fused_ms: float, probe_on: bool = True, reps: in
         if probe_on:
             m = probe.run([("launches dealt over two queues", probe.DealtRS(st.plan, [extra]), 0, 0)],
                           rsb, iters=40)["modes"][0]
+            # the probe deals over a stream of its own and `extra`: its rate
+            # alone shows whether those two had hardware queues of their own
             rec.update({"t_gemm_alone_ms": m["t_gemm_alone_ms"],
                         "t_gemm_concurrent_ms": m["t_gemm_concurrent_ms"],
-                        "gemm_slowdown_pct": m["gemm_slowdown_pct"]})
+                        "gemm_slowdown_pct": m["gemm_slowdown_pct"],
+                        "probe_rs_alone_gbps": m["rs_alone_gbps"],
+                        "probe_ran_concurrently": m["ran_concurrently"]})
     finally:
         torch.cuda.synchronize()
         api.tide_stream_destroy(extra)
