@@ -224,16 +224,14 @@ tide_status tide_rs_bf16_to_fp32_tiles(const void *h_plan, const void *d_plan,
  * the first waits for events of the others).  n_streams in [1, 64]; with
  * more than one stream none may be the null stream (TIDE_EINVAL: it
  * synchronises with every blocking stream, which would serialise the
- * launches; measured 72 ms against 19 ms for one stream).  HIP backs a
- * process's streams with a small pool of hardware queues (GPU_MAX_HW_QUEUES,
- * 4 by default), handed out in turn, so streams created far apart can
- * share one (CU-masked ones too), and launches dealt over streams on one
- * queue run one after the other.  Measured: two masked streams created one
- * right after the other kept 6.42-6.54 TB/s whatever the process created
- * before or after them (five ordinary streams), while one created before
- * and one after five ordinary streams shared a queue (5.90 TB/s, the
- * one-queue rate).  So create the streams to deal over one right after the
- * other. */
+ * launches; measured 72 ms against 19 ms for one stream).  The streams'
+ * creation order matters too: two masked streams created one right after
+ * the other kept 6.42-6.54 TB/s whatever the process created before or
+ * after them (five ordinary streams, used), while a pair created one before
+ * and one after five ordinary streams ran at 5.90 TB/s, the one-queue rate
+ * (the runtime then no longer ran the two side by side; the mechanism was
+ * not pinned down).  So create the streams to deal over one right after
+ * the other. */
 tide_status tide_rs_bf16_to_fp32_streams(const void *h_plan, const void *d_plan,
                                          int32_t order, int32_t max_workgroups,
                                          const tide_stream_t *streams, int32_t n_streams);
@@ -402,9 +400,9 @@ tide_status tide_stream_destroy(tide_stream_t stream);
  * floats, then moved to the shard arenas by phase 2 (phase2 = 0: the
  * tide_rs_stage_to_shards kernel; 1: the copy-kind copies of
  * tide_rs_stage_to_shards_sdma).  The phases run on two streams of the
- * pipeline object, created one right after the other so that each gets
- * a hardware queue of its own (see tide_rs_bf16_to_fp32_streams), ordered
- * per slot
+ * pipeline object, created one right after the other (see
+ * tide_rs_bf16_to_fp32_streams), each with a hardware queue of its own,
+ * ordered per slot
  * by events: phase 2 of chunk i after its phase 1, phase 1 of chunk i after
  * phase 2 of chunk i - depth.  The result is bit-identical to
  * tide_rs_bf16_to_fp32 with order 0.
