@@ -98,8 +98,11 @@ def run(modes: Sequence[Mode], rs_bytes: int, iters: int = 40, M: int = 4096, N:
     reduce-scatter always runs on a CU-masked stream, which HIP backs with a
     hardware queue of its own (with the full mask when the mode has none):
     two streams that share a hardware queue run one after the other, which
-    would hide any interference.  The heap is frozen and the garbage
-    collector paused meanwhile (quiet_gc=False leaves both alone)."""
+    would hide any interference.  Each mode's record says how many GEMMs
+    overlapped a reduce-scatter call's own span (gemms_overlapping_rs,
+    ran_concurrently), from events around every call.  The heap is frozen
+    and the garbage collector paused meanwhile (quiet_gc=False leaves both
+    alone)."""
     if not quiet_gc:
         return _run(modes, rs_bytes, iters, M, N, K)
     with _no_gc():
