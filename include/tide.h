@@ -420,8 +420,9 @@ tide_status tide_stream_destroy(tide_stream_t stream);
  * only with phase2_cus = 0.  Ordered after the earlier work of `stream` and
  * before its later work; asynchronous.  All checks are made before anything
  * is issued.  Calls on one object must not overlap in time from several
- * host threads; calls issued one after another on the same stream may
- * share the ring.  The object's streams are CU-masked, which HIP creates as
+ * host threads; calls issued one after another may share the ring, on the
+ * same stream or not (a slot is refilled only after the phase 2 that last
+ * drained it, also one of an earlier call).  The object's streams are CU-masked, which HIP creates as
  * blocking streams: calls issued back to back on the null stream, whose
  * pending work every blocking stream then waits on implicitly, measured up
  * to 20% slower than on another stream (or with the host waiting between

@@ -19,7 +19,9 @@
 //   s2: wait produced[i % depth];  phase 2 of chunk i;  record drained[i % depth]
 // A wait binds to the event's most recent record at the time the wait is
 // issued, and every wait is issued after the record it needs, so events are
-// reused across chunks and calls without a host synchronisation.
+// reused across chunks and calls without a host synchronisation.  A slot
+// drained by an earlier call is waited for in the next call too, so calls
+// issued on different streams can share the ring.
 // Host code only.
 #include <hip/hip_runtime.h>
 
@@ -46,6 +48,7 @@ struct tide_pipeline {
     hipStream_t s1 = nullptr, s2 = nullptr;
     hipEvent_t start = nullptr, done1 = nullptr, done2 = nullptr;
     std::vector<hipEvent_t> produced, drained;
+    std::vector<char> drained_once;  // slot k's drained event has been recorded
 };
 
 namespace {
@@ -122,6 +125,7 @@ extern "C" tide_status tide_pipeline_create(int32_t depth, int32_t phase2_cus,
     p->device = dev;
     p->depth = depth;
     p->phase2_cus = phase2_cus;
+    p->drained_once.assign((size_t)depth, 0);
     // phase 2 confined to CUs [0, phase2_cus), phase 1 to the rest; with
     // phase2_cus == 0 both streams may use every CU
     tide_stream_t s1 = nullptr, s2 = nullptr;
@@ -188,7 +192,8 @@ extern "C" tide_status tide_pipeline_run(tide_pipeline_t p, const void* h_plan,
         const int64_t cnt = chunk_tiles < n - b ? chunk_tiles : n - b;
         const int32_t k = (int32_t)(i % p->depth);
         float* buf = ring + k * slot;
-        if (i >= p->depth && hipStreamWaitEvent(p->s1, p->drained[k], 0) != hipSuccess) {
+        if ((i >= p->depth || p->drained_once[k]) &&
+            hipStreamWaitEvent(p->s1, p->drained[k], 0) != hipSuccess) {
             st = TIDE_EHIP;
             break;
         }
@@ -203,7 +208,10 @@ extern "C" tide_status tide_pipeline_run(tide_pipeline_t p, const void* h_plan,
         st = phase2 == 0 ? issue_stage_to_shards(h, d_plan, b, cnt, buf, 0, s2)
                          : issue_stage_to_shards_sdma(h, h_plan, b, cnt, buf, s2);
         if (st != TIDE_OK) break;
-        if (hipEventRecord(p->drained[k], p->s2) != hipSuccess) st = TIDE_EHIP;
+        if (hipEventRecord(p->drained[k], p->s2) != hipSuccess)
+            st = TIDE_EHIP;
+        else
+            p->drained_once[k] = 1;
     }
     // the caller's stream waits for both phases, also after a failure, so
     // that its later work never races whatever was issued

@@ -190,3 +190,45 @@ def test_prequeued_timing_of_a_pipelined_call():
     assert r["prequeued_ms"] is not None
     assert 0.25 * r["plain_ms"] <= r["prequeued_ms"] <= 4.0 * r["plain_ms"] + 1.0, r
     gu.check_rs_full(st)
+
+
+def test_ring_shared_by_calls_on_two_streams():
+    """One pipeline object and one ring, two calls issued on two streams with
+    nothing ordering them: each call's chunks wait for the phase 2 that last
+    drained their slot, also the other call's, so both results are the
+    oracle's (two plans over the same gradients with arenas of their own, so
+    that a slot refilled too early would leave wrong words behind).  Phase 2
+    on 8 CUs lags phase 1, which is what exposes a slot refilled while the
+    other call still drains it: before each chunk waited for its slot's last
+    drain from an earlier call too, this case left about a million wrong
+    words in the first call's arenas."""
+    shapes = [(16384, 1024)]
+    R = 8
+    w = _wl(shapes, R, 970, sigma=1e-3)
+    st = harness.setup(w, with_ag=False)
+    st.plan.rs()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in st.out]
+    out2 = [torch.empty(st.S, dtype=torch.float32, device="cuda") for _ in range(R)]
+    plan2 = api.Plan(w.shapes, R, grads=st.grads, out=out2)
+    chunk, depth = 512, 2
+    T = int(st.plan.info.rs_tile_elems)
+    assert -(-int(st.plan.info.rs_tiles) // chunk) > 4 * depth
+    ring = torch.empty(depth * chunk * T, dtype=torch.float32, device="cuda")
+    h = api.tide_pipeline_create(depth, 8)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        for _ in range(3):
+            for o in st.out + out2:
+                o.view(torch.int32).fill_(-1)
+            torch.cuda.synchronize()
+            gu.say("ring shared by two streams")
+            api.tide_pipeline_run(h, st.plan.blob, st.plan.d_blob, chunk, ring, 0, stream=sa)
+            api.tide_pipeline_run(h, plan2.blob, plan2.d_blob, chunk, ring, 0, stream=sb)
+            torch.cuda.synchronize()
+            for r in range(R):
+                assert torch.equal(st.out[r].view(torch.int32), ref[r].view(torch.int32)), r
+                assert torch.equal(out2[r].view(torch.int32), ref[r].view(torch.int32)), r
+    finally:
+        torch.cuda.synchronize()
+        api.tide_pipeline_destroy(h)
