@@ -568,28 +568,36 @@ RsKernel pick_nt(uint32_t flags) {
 
 // Rank batching: small power-of-two R loads every rank at once (with U
 // chunks per lane when R < 8 and the tile holds them, so that up to 8 loads
-// are in flight); R a multiple of 8 loads 8 ranks per batch; anything else
-// batches 8, the last batch re-reading a rank in place of the missing ones.  Measured on MI355X: a second chunk per lane at R = 8 did not help
-// (5.6 vs 5.8 TB/s); batches of 8 beat batches of 16 at R = 16..64 by 1-3%.
-// Chunks per lane for R < 8: as many as the tile holds, up to 4 (a chunk
-// past the tile end would only re-read its start).
+// are in flight).  R a multiple of 8 loads 2 ranks per batch, or 4 when the
+// launch holds two workgroups per CU (the plan's LDS reservation): about
+// 32-48 KB of loads in flight per CU read fastest.  Measured on MI355X
+// (same buffers, one process, two processes each): against batches of 8,
+// +1.5..2.1% at R = 8, +1.0..1.6% at R = 16, +1.5..2.3% at R = 32 (2 ranks
+// per batch, 5-6 workgroups per CU) and +1.6..1.9% at R = 64 (4 ranks, 2
+// per CU); 2 ranks at R = 64 read 14% less, 16 ranks 1.5-3.2% less than 8.
+// Any other R batches 8, the last batch re-reading a rank in place of the
+// missing ones.  Chunks per lane for R < 8: as many as the tile holds, up
+// to 4 (a chunk past the tile end would only re-read its start); a second
+// chunk per lane at R = 8 did not help (5.6 vs 5.8 TB/s).
 template <typename K, K (*PICK1)(uint32_t), K (*PICK2)(uint32_t), K (*PICK4)(uint32_t)>
 K by_chunks(int32_t tile, uint32_t flags) {
     const int32_t chunks = tile / kTileQuantum;
     return chunks >= 4 ? PICK4(flags) : chunks >= 2 ? PICK2(flags) : PICK1(flags);
 }
 
-RsKernel pick_fixed(int R, uint32_t flags, int32_t tile) {
+RsKernel pick_fixed(int R, uint32_t flags, int32_t tile, bool two_per_cu) {
     switch (R) {
         case 1: return by_chunks<RsKernel, pick_nt<1, true, 1>, pick_nt<1, true, 2>, pick_nt<1, true, 4>>(tile, flags);
         case 2: return by_chunks<RsKernel, pick_nt<2, true, 1>, pick_nt<2, true, 2>, pick_nt<2, true, 4>>(tile, flags);
         case 4: return by_chunks<RsKernel, pick_nt<4, true, 1>, pick_nt<4, true, 2>, pick_nt<4, true, 4>>(tile, flags);
-        case 8: return pick_nt<8, true, 1>(flags);
         default: break;
     }
-    if (R % 8 == 0) return pick_nt<8, true, 1>(flags);
+    if (R % 8 == 0) return two_per_cu ? pick_nt<4, true, 1>(flags) : pick_nt<2, true, 1>(flags);
     return pick_nt<8, false, 1>(flags);
 }
+
+// A launch holds two workgroups per CU when the plan reserves LDS for them.
+bool holds_two_per_cu(const PlanHeader& h) { return h.rs_lds_bytes > (uint32_t)kRsStaticLds; }
 
 template <int LEVELS>
 RsKernel pick_tree_nt(uint32_t flags) {
@@ -618,14 +626,14 @@ DenseKernel pick_dense_nt(uint32_t flags) {
     return rs_dense_kernel<RB, EXACT, U, false, false>;
 }
 
-DenseKernel pick_dense(int R, uint32_t flags, int32_t tile) {
+DenseKernel pick_dense(int R, uint32_t flags, int32_t tile, bool two_per_cu) {
     switch (R) {
         case 1: return by_chunks<DenseKernel, pick_dense_nt<1, true, 1>, pick_dense_nt<1, true, 2>, pick_dense_nt<1, true, 4>>(tile, flags);
         case 2: return by_chunks<DenseKernel, pick_dense_nt<2, true, 1>, pick_dense_nt<2, true, 2>, pick_dense_nt<2, true, 4>>(tile, flags);
         case 4: return by_chunks<DenseKernel, pick_dense_nt<4, true, 1>, pick_dense_nt<4, true, 2>, pick_dense_nt<4, true, 4>>(tile, flags);
         default: break;
     }
-    if (R % 8 == 0) return pick_dense_nt<8, true, 1>(flags);
+    if (R % 8 == 0) return two_per_cu ? pick_dense_nt<4, true, 1>(flags) : pick_dense_nt<2, true, 1>(flags);
     return pick_dense_nt<8, false, 1>(flags);
 }
 
@@ -642,14 +650,14 @@ FoldKernel pick_fold_nt(uint32_t flags) {
 }
 
 // Same rank batching as the in-place kernels.
-FoldKernel pick_fold(int R, uint32_t flags, int32_t tile) {
+FoldKernel pick_fold(int R, uint32_t flags, int32_t tile, bool two_per_cu) {
     switch (R) {
         case 1: return by_chunks<FoldKernel, pick_fold_nt<1, true, 1>, pick_fold_nt<1, true, 2>, pick_fold_nt<1, true, 4>>(tile, flags);
         case 2: return by_chunks<FoldKernel, pick_fold_nt<2, true, 1>, pick_fold_nt<2, true, 2>, pick_fold_nt<2, true, 4>>(tile, flags);
         case 4: return by_chunks<FoldKernel, pick_fold_nt<4, true, 1>, pick_fold_nt<4, true, 2>, pick_fold_nt<4, true, 4>>(tile, flags);
         default: break;
     }
-    if (R % 8 == 0) return pick_fold_nt<8, true, 1>(flags);
+    if (R % 8 == 0) return two_per_cu ? pick_fold_nt<4, true, 1>(flags) : pick_fold_nt<2, true, 1>(flags);
     return pick_fold_nt<8, false, 1>(flags);
 }
 
@@ -705,7 +713,8 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     const uint64_t* obase = reinterpret_cast<const uint64_t*>(d + h.off_obase);
     int R = h.R;
-    RsKernel k = order == 0 ? pick_fixed(R, h.flags, h.rs_tile) : pick_tree(R, h.flags);
+    RsKernel k = order == 0 ? pick_fixed(R, h.flags, h.rs_tile, holds_two_per_cu(h))
+                            : pick_tree(R, h.flags);
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
 
     // One launch per run of per_launch tiles: the launch boundaries are where
@@ -780,7 +789,8 @@ extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_pla
     int R = h.R;
     int vec = vec_ok ? 1 : 0;
     int64_t stride = 2 * slot_stride;
-    FoldKernel k = order == 0 ? pick_fold(R, h.flags, h.rs_tile) : pick_fold_tree(R, h.flags);
+    FoldKernel k = order == 0 ? pick_fold(R, h.flags, h.rs_tile, holds_two_per_cu(h))
+                              : pick_fold_tree(R, h.flags);
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : h.n_rs_tiles;
     for (int64_t b = 0; b < h.n_rs_tiles; b += per_launch) {
         const RsTile* tiles = all + b;
@@ -807,7 +817,7 @@ tide_status issue_tiles_to_stage(const PlanHeader& h, const void* d_plan, int64_
     const uint64_t* gptr = reinterpret_cast<const uint64_t*>(d + h.off_gptr);
     int R = h.R;
     int64_t T = h.rs_tile;
-    DenseKernel k = pick_dense(R, h.flags, h.rs_tile);
+    DenseKernel k = pick_dense(R, h.flags, h.rs_tile, holds_two_per_cu(h));
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
     for (int64_t b = tile_begin; b < tile_begin + tile_count; b += per_launch) {
         const RsTile* tiles = all + b;
