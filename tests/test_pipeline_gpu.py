@@ -50,6 +50,24 @@ def test_phases_in_sequence_bitwise(R, shapes):
     gu.check_rs_full(st)
 
 
+@pytest.mark.parametrize("R", [8, 12, 16, 64])
+@pytest.mark.parametrize("launch", ["reserving", "one"])
+def test_phase1_rank_batching_variants_bitwise(R, launch):
+    """Phase 1 in every rank-batching form (4 ranks per batch in launches
+    that reserve LDS, 2 otherwise, 8 with a re-read rank when R is not a
+    multiple of 8), then phase 2: the oracle's bits."""
+    w = _wl([(2 * R + 3, 40), (R - 1, 8), (4096, 16)], R, 960 + R, sigma=1e-3)
+    st = harness.setup(w, with_ag=False, launch_mib=-1 if launch == "one" else 0)
+    assert (st.plan.info.rs_lds_bytes > 8192) == (launch == "reserving")
+    n, T = int(st.plan.info.rs_tiles), int(st.plan.info.rs_tile_elems)
+    stage = torch.empty(max(1, n) * T, dtype=torch.float32, device="cuda")
+    gu.say("pipeline phase-1 batching", R, launch)
+    api.tide_rs_tiles_to_stage(st.plan.blob, st.plan.d_blob, 0, n, stage)
+    api.tide_rs_stage_to_shards(st.plan.blob, st.plan.d_blob, 0, n, stage)
+    torch.cuda.synchronize()
+    gu.check_rs_full(st)
+
+
 @pytest.mark.parametrize("chunk,depth,phase2,cus", [(1, 1, "cu", 0), (7, 2, "cu", 0), (64, 3, "cu", 0),
                                                     (10 ** 6, 1, "cu", 0), (7, 2, "cu", 8),
                                                     (1, 2, "sdma", 0), (7, 2, "sdma", 0),

@@ -139,6 +139,23 @@ def test_fuzz_random_problems(seed):
     gu.check_rs_full(st, order)
 
 
+@pytest.mark.parametrize("R", [8, 12, 16, 20, 24, 40, 64, 72])
+@pytest.mark.parametrize("launch", ["reserving", "one"])
+def test_rank_batching_variants_bitwise(R, launch):
+    """Every rank-batching form of the fixed-order kernel against the oracle:
+    R a multiple of 8 loads 4 ranks per batch in launches that reserve LDS
+    (a small layer's default plan: at most 2 workgroups per CU) and 2 ranks
+    per batch otherwise (one unrounded launch); other R load 8 per batch, the
+    last batch re-reading a rank.  Ragged and all-padding shards included."""
+    w = _wl([(2 * R + 3, 40), (R - 1, 8), (4096, 16)], R, key=260 + R, sigma=1e-3)
+    gu.say("batching R", R, launch)
+    st = harness.setup(w, with_ag=False, launch_mib=-1 if launch == "one" else 0)
+    reserving = st.plan.info.rs_lds_bytes > 8192
+    assert reserving == (launch == "reserving"), st.plan.info.rs_lds_bytes
+    _run(st)
+    gu.check_rs_full(st)
+
+
 @pytest.mark.parametrize("align", [4, 8, 64])
 def test_aligned_offsets_leave_gaps(align):
     w = _wl([(37, 16), (5,), (3, 3), (40, 8)], 4, key=131)

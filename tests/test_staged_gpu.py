@@ -65,6 +65,20 @@ def test_ragged_shapes_bitwise(R, shapes, order):
     gu.check_rs_full(st, order)
 
 
+@pytest.mark.parametrize("R", [8, 12, 16, 64])
+@pytest.mark.parametrize("launch", ["reserving", "one"])
+def test_fold_rank_batching_variants_bitwise(R, launch):
+    """The fold in every rank-batching form (4 ranks per batch in launches
+    that reserve LDS, 2 otherwise, 8 with a re-read rank when R is not a
+    multiple of 8): the oracle's bits."""
+    w = _wl([(2 * R + 3, 40), (R - 1, 8), (4096, 16)], R, 860 + R, sigma=1e-3)
+    st = harness.setup(w, with_ag=False, launch_mib=-1 if launch == "one" else 0)
+    assert (st.plan.info.rs_lds_bytes > 8192) == (launch == "reserving")
+    gu.say("staged fold batching", R, launch)
+    _staged(st, harness.stage_buffers(st))
+    gu.check_rs_full(st)
+
+
 @pytest.mark.parametrize("stride_extra,offset", [(13, 0), (0, 3), (64, 8)])
 def test_unaligned_or_padded_slots(stride_extra, offset):
     """Slot strides that are not a multiple of 8 elements or buffers that do
