@@ -418,6 +418,29 @@ __global__ __launch_bounds__(kBlock) void rs_tree_kernel(const RsTile* __restric
 }
 
 template <int RB, bool EXACT, int U, bool NTL, bool NTS>
+__device__ __forceinline__ void rs_fixed_tile(const RsTile* __restrict__ tiles, int64_t t,
+                                              const uint64_t* __restrict__ gptr,
+                                              const uint64_t* __restrict__ obase, int R,
+                                              uint32_t* __restrict__ census,
+                                              uint64_t* __restrict__ stamps, float* lds_wave) {
+    if (census && threadIdx.x == 0) census[t] = hw_cu_id();
+    const uint64_t t_begin = stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+    const RsTile tile = tiles[t];
+    float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
+    const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
+    if (tile.kind == kRsVec)
+        rs_vec_fixed<RB, EXACT, U, NTL, NTS>(src, R, tile.len, out, lds_wave);
+    else if (tile.kind == kRsScalar)
+        rs_scalar_fixed(src, R, tile.len, out);
+    else
+        rs_pad(tile.len, out);
+    stamp_tile(stamps, t, t_begin);
+}
+
+// SKEW: the instance for launches of skewed_grid(ntiles) workgroups, each
+// taking one tile at most (xcd_map.h); the plain instance runs one
+// workgroup per tile or a capped grid striding over the tiles.
+template <int RB, bool EXACT, int U, bool NTL, bool NTS, bool SKEW = false>
 __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restrict__ tiles,
                                                           int64_t ntiles,
                                                           const uint64_t* __restrict__ gptr,
@@ -426,20 +449,17 @@ __global__ __launch_bounds__(kBlock) void rs_fixed_kernel(const RsTile* __restri
                                                           uint64_t* __restrict__ stamps) {
     __shared__ float lds[kBlock * kVec];
     float* lds_wave = lds + (threadIdx.x & ~63) * kVec;
-    for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
-        const int64_t t = tile_of(b, ntiles);
-        if (census && threadIdx.x == 0) census[t] = hw_cu_id();
-        const uint64_t t_begin = stamps ? __builtin_amdgcn_s_memrealtime() : 0;
-        const RsTile tile = tiles[t];
-        float* out = reinterpret_cast<float*>(obase[tile.r]) + tile.o0;
-        const GradSrc src{gptr + (int64_t)tile.p * R, tile.j0};
-        if (tile.kind == kRsVec)
-            rs_vec_fixed<RB, EXACT, U, NTL, NTS>(src, R, tile.len, out, lds_wave);
-        else if (tile.kind == kRsScalar)
-            rs_scalar_fixed(src, R, tile.len, out);
-        else
-            rs_pad(tile.len, out);
-        stamp_tile(stamps, t, t_begin);
+    if constexpr (SKEW) {
+        for (int64_t b = blockIdx.x; b < walk_end(ntiles); b += gridDim.x) {
+            const int64_t t = tile_of_skewed(b, ntiles);
+            if (t < 0) continue;
+            rs_fixed_tile<RB, EXACT, U, NTL, NTS>(tiles, t, gptr, obase, R, census, stamps,
+                                                  lds_wave);
+        }
+    } else {
+        for (int64_t b = blockIdx.x; b < ntiles; b += gridDim.x)
+            rs_fixed_tile<RB, EXACT, U, NTL, NTS>(tiles, tile_of(b, ntiles), gptr, obase, R,
+                                                  census, stamps, lds_wave);
     }
 }
 
@@ -558,13 +578,13 @@ __global__ __launch_bounds__(kBlock) void rs_drain_kernel(const RsTile* __restri
 typedef void (*RsKernel)(const RsTile*, int64_t, const uint64_t*, const uint64_t*, int, uint32_t*,
                          uint64_t*);
 
-template <int RB, bool EXACT, int U>
+template <int RB, bool EXACT, int U, bool SKEW = false>
 RsKernel pick_nt(uint32_t flags) {
     const bool ntl = flags & kFlagNtLoads, nts = flags & kFlagNtStores;
-    if (ntl && nts) return rs_fixed_kernel<RB, EXACT, U, true, true>;
-    if (ntl) return rs_fixed_kernel<RB, EXACT, U, true, false>;
-    if (nts) return rs_fixed_kernel<RB, EXACT, U, false, true>;
-    return rs_fixed_kernel<RB, EXACT, U, false, false>;
+    if (ntl && nts) return rs_fixed_kernel<RB, EXACT, U, true, true, SKEW>;
+    if (ntl) return rs_fixed_kernel<RB, EXACT, U, true, false, SKEW>;
+    if (nts) return rs_fixed_kernel<RB, EXACT, U, false, true, SKEW>;
+    return rs_fixed_kernel<RB, EXACT, U, false, false, SKEW>;
 }
 
 // Rank batching: small power-of-two R loads every rank at once (with U
@@ -599,6 +619,14 @@ RsKernel pick_fixed(int R, uint32_t flags, int32_t tile, bool two_per_cu) {
 
 // A launch holds two workgroups per CU when the plan reserves LDS for them.
 bool holds_two_per_cu(const PlanHeader& h) { return h.rs_lds_bytes > (uint32_t)kRsStaticLds; }
+
+// The skewed form (xcd_map.h) of the fixed-order kernel that loads 2 ranks
+// per batch, for launches of kSkewMinTiles tiles or more; null where the
+// plan's kernel has none (other rank counts were not measured with it).
+RsKernel pick_fixed_skewed(int R, uint32_t flags, bool two_per_cu) {
+    if (R % 8 == 0 && !two_per_cu) return pick_nt<2, true, 1, true>(flags);
+    return nullptr;
+}
 
 template <int LEVELS>
 RsKernel pick_tree_nt(uint32_t flags) {
@@ -716,6 +744,9 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
     int R = h.R;
     RsKernel k = order == 0 ? pick_fixed(R, h.flags, h.rs_tile, holds_two_per_cu(h))
                             : pick_tree(R, h.flags);
+    RsKernel ks = order == 0 && max_workgroups == 0
+                      ? pick_fixed_skewed(R, h.flags, holds_two_per_cu(h))
+                      : nullptr;
     const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
 
     // One launch per run of per_launch tiles: the launch boundaries are where
@@ -725,13 +756,15 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
         const RsTile* tiles = all + b;
         int64_t ntiles = per_launch < tile_begin + tile_count - b ? per_launch
                                                                   : tile_begin + tile_count - b;
-        int64_t grid = ntiles;
+        const bool skew = ks && ntiles >= kSkewMinTiles && skewed_grid(ntiles) <= INT_MAX;
+        int64_t grid = skew ? skewed_grid(ntiles) : ntiles;
         if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
         if (grid > INT_MAX) grid = INT_MAX;
         uint32_t* cen = census ? census + (b - tile_begin) : nullptr;
         uint64_t* stp = stamps ? stamps + 2 * (b - tile_begin) : nullptr;
         void* args[] = {&tiles, &ntiles, &gptr, &obase, &R, &cen, &stp};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)grid),
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(skew ? ks : k),
+                                       dim3((unsigned)grid),
                                        dim3(kBlock), args, rs_extra_lds(h),
                                        reinterpret_cast<hipStream_t>(streams[i % n_streams]));
         if (e != hipSuccess) return TIDE_EHIP;

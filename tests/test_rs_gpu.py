@@ -156,6 +156,40 @@ def test_rank_batching_variants_bitwise(R, launch):
     gu.check_rs_full(st)
 
 
+@pytest.mark.parametrize("R", [8, 16])
+def test_skewed_launches_bitwise(R):
+    """Launches of 2048 tiles or more at R a multiple of 8 (2 ranks per
+    batch) run the skewed XCD mapping, in which the odd XCDs' spare
+    workgroups take no tile: at R = 8 one skewed launch of 2425 tiles, at
+    R = 16 two of 2275 and a plain one of 299.  Whole arenas against the
+    oracle; the per-tile trace stamps every tile exactly once with the same
+    bits; a capped grid (no skew) gives the same bits."""
+    w = _wl([(300 * R + 3, 2048), (R - 1, 8), (333, 40)], R, key=280 + R, sigma=1e-3)
+    gu.say("skewed launches R", R)
+    st = harness.setup(w, with_ag=False)
+    info = st.plan.info
+    assert info.rs_lds_bytes == 8192 and info.rs_launch_tiles >= 2048
+    _run(st)
+    gu.check_rs_full(st)
+    ref = [o.clone() for o in st.out]
+
+    def same():
+        return all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(st.out, ref))
+
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    census, stamps = st.plan.rs_trace()
+    torch.cuda.synchronize()
+    assert same()
+    c, s = census.cpu().numpy(), stamps.cpu().numpy()
+    assert c.size == info.rs_tiles and (c >= 0).all()
+    assert (s[:, 0] > 0).all() and (s[:, 1] >= s[:, 0]).all()
+    for o in st.out:
+        o.view(torch.int32).fill_(-1)
+    _run(st, max_wg=1000)
+    assert same()
+
+
 @pytest.mark.parametrize("align", [4, 8, 64])
 def test_aligned_offsets_leave_gaps(align):
     w = _wl([(37, 16), (5,), (3, 3), (40, 8)], 4, key=131)
