@@ -616,8 +616,10 @@ def trace_leg(st, max_wg: int):
     te1.record()
     torch.cuda.synchronize()
     ids = census.cpu().numpy()
-    cu_rec = profiling.cu_time(ids, stamps.cpu().numpy())
+    st_np = stamps.cpu().numpy()
+    cu_rec = profiling.cu_time(ids, st_np)
     cu_rec["traced_call_ms_events"] = round(te0.elapsed_time(te1), 4)
+    cu_rec["workgroup_us_by_xcc"] = profiling.workgroup_us_by_xcc(ids, st_np)
     per_xcc = {}
     for v in set(ids.tolist()):
         per_xcc[v >> 8] = per_xcc.get(v >> 8, 0) + 1

@@ -304,6 +304,24 @@ def cu_time(census, stamps, tick_hz: float = 1e8) -> dict:
             "tick_hz": tick_hz}
 
 
+def workgroup_us_by_xcc(census, stamps, tick_hz: float = 1e8) -> dict:
+    """Mean workgroup duration (microseconds) per XCC from the same trace:
+    the packed census id carries the XCC in bits [8, 12).  On the MI355X the
+    odd-numbered XCCs run the reduce-scatter's workgroups several percent
+    longer than the even-numbered ones.  Keys are XCC ids as strings."""
+    import numpy as np
+
+    cu = np.asarray(census).astype(np.int64).reshape(-1)
+    st = np.asarray(stamps).astype(np.int64).reshape(-1, 2)
+    if cu.size == 0:
+        return {}
+    if np.any(st[:, 1] < st[:, 0]):
+        raise ValueError("a tile ends before it starts")
+    xcc = (cu >> 8) & 0xF
+    dur = (st[:, 1] - st[:, 0]) * (1e6 / tick_hz)
+    return {str(int(x)): round(float(dur[xcc == x].mean()), 3) for x in np.unique(xcc)}
+
+
 def _union(iv):
     """Total length of a union of (start, end) intervals, and the merged list."""
     out, total = [], 0

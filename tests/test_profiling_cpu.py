@@ -2,6 +2,8 @@
 import csv
 import json
 
+import pytest
+
 from shard_placement_amd import profiling
 
 
@@ -70,6 +72,19 @@ def test_cu_time_rejects_reversed_intervals():
 
     with pytest.raises(ValueError):
         cu_time([0], [[5, 4]])
+
+
+def test_workgroup_us_by_xcc():
+    from shard_placement_amd.profiling import workgroup_us_by_xcc
+
+    # tiles on XCC 0 (ids 0x005, 0x00a) last 10 and 20 ticks, on XCC 3
+    # (id 0x301) 40 ticks; 1 tick = 1 us
+    census = [0x005, 0x301, 0x00A]
+    stamps = [[0, 10], [5, 45], [100, 120]]
+    assert workgroup_us_by_xcc(census, stamps, tick_hz=1e6) == {"0": 15.0, "3": 40.0}
+    assert workgroup_us_by_xcc([], []) == {}
+    with pytest.raises(ValueError):
+        workgroup_us_by_xcc([0], [[5, 4]])
 
 
 def test_pipeline_phases_from_a_trace(tmp_path):
