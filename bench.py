@@ -759,9 +759,10 @@ def main():
 
     # The heap is frozen after setup and the collector stays paused from here
     # on, as timeit does while timing: a full collection walks every tracked
-    # object (~170 K here, ~20 ms of one core), and that walk alone, freeing
-    # nothing and making no HIP call, lengthened the single-wave GEMM by
-    # 10-15% in the interference probe; the host-timed legs (copy engines,
+    # object (~170 K here, 20-35 ms of one core) holding the interpreter lock,
+    # so this thread stops issuing GPU work; the GPU idles, and kernels issued
+    # after an idle stretch run slower for a while (the single-wave GEMM of
+    # the interference probe by 10-25%); the host-timed legs (copy engines,
     # pipeline issue) would absorb its pauses too.
     gc.collect()
     gc.freeze()

@@ -40,16 +40,21 @@ def _no_gc():
     """The heap frozen and the collector paused while timing.
 
     A full collection walks every tracked Python object (about 170 K in a
-    process holding torch and this package: 18-24 ms of one core).  Measured
-    on the R = 64 layer with a side thread collecting every 20 ms during the
-    probe: the walk alone, with nothing to free and no HIP call made by the
-    collecting thread, stretched the single-wave GEMM from 0.20 to 0.23-0.24
-    ms, alone and beside the reduce-scatter (+14.5..17% instead of
-    +3.6..3.8%).  After gc.freeze() the same collections take 0.02 ms and
-    the reading is the quiet one (+3.2..4.8%).  So the heap is frozen here
-    (any collection in the window has almost nothing to walk), and the
-    collector is also paused, as Python's timeit does; both are restored on
-    exit."""
+    process holding torch and this package: 18-35 ms of one core) and keeps
+    the interpreter lock for the whole walk, so the thread that issues GPU
+    work stops for that long.  The GPU runs out of queued work and idles,
+    and kernels issued after an idle stretch of 10 ms or more run slower
+    for a while (the single-wave GEMM: a median of 219-225 us against 201-206
+    right after other work, up to +25% ten to twenty GEMMs in; see
+    gemm_after_idle).  Measured on the R = 64 layer with a side thread acting
+    every 20 ms during the probe: collections, or a 30 ms sleep that keeps
+    the lock and touches no memory, stretched the GEMM from 0.20-0.21 to up
+    to 0.24-0.25 ms, alone or beside the reduce-scatter depending on where
+    the stall fell (readings -7..+22% instead of +3..5%); after gc.freeze()
+    the collections take 0.02 ms and the reading is the quiet one.  So the
+    heap is frozen here (any collection in the window has almost nothing to
+    walk), and the collector is also paused, as Python's timeit does; both
+    are restored on exit."""
     was = gc.isenabled()
     gc.collect()
     gc.freeze()
@@ -228,10 +233,42 @@ def _gemm_during(host_call, expect_ms, M, N, K) -> Dict:
             "gemm_slowdown_during_staging_pct": round(100.0 * (t1 / t0 - 1.0), 2)}
 
 
+def gemm_after_idle(idle_ms: Sequence[float] = (0, 2, 10, 30, 100, 300), n: int = 60,
+                    rounds: int = 2, M: int = 4096, N: int = 4096, K: int = 8192) -> List[Dict]:
+    """The single-wave GEMM train issued after the GPU sat idle (nothing
+    queued, the host asleep) for idle_ms: the median per-GEMM time and the
+    mean of each group of five by position in the train, in microseconds."""
+    import time
+
+    dev = torch.device("cuda")
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+    s = _new_stream()
+    out = []
+    with _no_gc():
+        for _ in range(2):
+            _gemm_train(a, b, c, s, n)
+            torch.cuda.synchronize()
+        for _ in range(rounds):
+            for idle in idle_ms:
+                torch.cuda.synchronize()
+                time.sleep(idle / 1e3)
+                evs = _gemm_train(a, b, c, s, n)
+                torch.cuda.synchronize()
+                t = [1e3 * e0.elapsed_time(e1) for e0, e1 in evs]
+                out.append({"idle_ms": idle, "median_us": round(_median(t), 1),
+                            "us_by_position_of_5": [round(sum(t[i:i + 5]) / len(t[i:i + 5]), 1)
+                                                    for i in range(0, len(t), 5)]})
+    return out
+
+
 def main(argv=None) -> int:
     """Standalone probe: set up one layer (reduce-scatter buffers only) and
     run the default-launch probe ``--reps`` times in this process; prints
-    one JSON line {"workload": ..., "probe": {...}} with every repetition."""
+    one JSON line {"workload": ..., "probe": {...}} with every repetition.
+    With --after-idle: only the GEMM trains after idle stretches
+    (gemm_after_idle), one JSON line per train."""
     import argparse
     import json
 
@@ -241,12 +278,20 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="5", help="workload key or name")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--iters", type=int, default=40)
-    ap.add_argument("--side", default="none", choices=("none", "collect", "collect-frozen", "trim"),
+    ap.add_argument("--side", default="none",
+                    choices=("none", "collect", "collect-frozen", "trim", "hold-lock"),
                     help="a side thread acting every 20 ms during the probe: a full garbage "
-                         "collection, the same after gc.freeze(), or malloc_trim(0)")
+                         "collection, the same after gc.freeze(), malloc_trim(0), or a 30 ms "
+                         "sleep that keeps the interpreter lock")
+    ap.add_argument("--after-idle", action="store_true",
+                    help="time GEMM trains issued after the GPU idled 0-300 ms instead")
     a = ap.parse_args(argv)
     if not torch.cuda.is_available():
         raise SystemExit("the probe needs a GPU")
+    if a.after_idle:
+        for rec in gemm_after_idle():
+            print(json.dumps(rec), flush=True)
+        return 0
     w = configs.get(a.workload)
     st = harness.setup(w, with_ag=False)
     torch.cuda.synchronize()
@@ -268,8 +313,11 @@ def main(argv=None) -> int:
 class _Side:
     """A thread that, every 20 ms until stopped, runs a full garbage
     collection ("collect"), the same after freezing the heap once
-    ("collect-frozen"), or glibc's malloc_trim(0) ("trim"); collections are
-    logged through gc.callbacks."""
+    ("collect-frozen"), glibc's malloc_trim(0) ("trim"), or a 30 ms usleep
+    called through ctypes.PyDLL, which keeps the interpreter lock for the
+    whole call and touches no memory ("hold-lock": a collection also keeps
+    the lock for its whole walk, while a Python-level busy loop would give it
+    up every switch interval); collections are logged through gc.callbacks."""
 
     def __init__(self, mode: str):
         import ctypes
@@ -284,6 +332,8 @@ class _Side:
             gc.freeze()
         self._stop = threading.Event()
         libc = ctypes.CDLL("libc.so.6") if mode == "trim" else None
+        # PyDLL: the call runs with the interpreter lock held
+        locked = ctypes.PyDLL("libc.so.6") if mode == "hold-lock" else None
 
         def loop():
             while not self._stop.is_set():
@@ -293,6 +343,8 @@ class _Side:
                     gc.collect()
                 elif mode == "trim":
                     libc.malloc_trim(0)
+                elif mode == "hold-lock":
+                    locked.usleep(30000)
                 self.took.append(time.perf_counter() - t)
         self._th = threading.Thread(target=loop, daemon=True)
         if mode != "none":
