@@ -58,3 +58,23 @@ def test_side_thread_collects_and_reports():
     s = probe._Side("none")
     s.stop()
     assert s.report()["calls"] == 0
+
+
+def test_hold_lock_side_thread_stalls_this_thread():
+    """The hold-lock side thread keeps the interpreter lock through its
+    30 ms sleeps: this thread, ticking every millisecond, sees gaps of about
+    that length (a Python busy loop would give the lock up every switch
+    interval)."""
+    import time
+
+    s = probe._Side("hold-lock")
+    ticks = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        ticks.append(time.perf_counter())
+        time.sleep(0.001)
+    s.stop()
+    gaps = [b - a for a, b in zip(ticks, ticks[1:])]
+    assert max(gaps) >= 0.025
+    r = s.report()
+    assert r["mode"] == "hold-lock" and r["calls"] >= 1
