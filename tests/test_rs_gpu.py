@@ -401,14 +401,19 @@ def test_cu_census_same_bits_and_counts():
         api.tide_stream_destroy(s)
 
 
-@pytest.mark.parametrize("R,shapes", [(8, [(4096, 256), (7,), (130, 24)]),
-                                      (64, [(4096, 1024), (1001, 64), (128,)])], ids=["8", "64"])
-def test_launches_dealt_over_streams_same_bits(R, shapes):
+@pytest.mark.parametrize("R,shapes,launch_mib", [(8, [(4096, 256), (7,), (130, 24)], 8),
+                                                 (64, [(4096, 1024), (1001, 64), (128,)], 8),
+                                                 (8, [(4096, 3072), (7,), (130, 24)], 80)],
+                         ids=["8", "64", "8-skewed"])
+def test_launches_dealt_over_streams_same_bits(R, shapes, launch_mib):
     """tide_rs_bf16_to_fp32_streams: the launches over 1, 2 or 3 CU-masked
-    streams (hardware queues of their own) give the oracle's bits."""
+    streams (hardware queues of their own) give the oracle's bits, also when
+    the launches are skewed (2048 tiles each at R = 8 with 80 MiB)."""
     w = _wl(shapes, R, key=175 + R, sigma=1e-3)
-    st = harness.setup(w, with_ag=False, guard=64, launch_mib=8)
+    st = harness.setup(w, with_ag=False, guard=64, launch_mib=launch_mib)
     assert -(-int(st.plan.info.rs_tiles) // int(st.plan.info.rs_launch_tiles)) >= 3
+    if launch_mib == 80:
+        assert st.plan.info.rs_launch_tiles == 2048
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     extra = [api.tide_stream_create_cu_limited(ncu) for _ in range(3)]
     try:
