@@ -63,7 +63,9 @@ __device__ __forceinline__ int64_t walk_end(int64_t ntiles) {
 }
 
 // Workgroup -> tile (or -1) for a grid of skewed_grid(ntiles) workgroups;
-// a grid of ntiles workgroups maps as tile_of, a smaller one strides.
+// a grid of ntiles workgroups maps as tile_of, a smaller one strides.  A
+// grid larger than ntiles must be skewed_grid(ntiles) with ntiles >=
+// kXcdSpan (the launch code only makes it for ntiles >= kSkewMinTiles).
 __device__ __forceinline__ int64_t tile_of_skewed(int64_t b, int64_t ntiles) {
     const int64_t g = gridDim.x;
     if (g < ntiles) return b;
