@@ -78,6 +78,18 @@ constexpr int32_t kDefaultRsLaunchMiB = 160;
 constexpr int64_t kCuTiles = 256;
 constexpr int64_t kRsRoundBelowTiles = 4 * kCuTiles;
 constexpr int64_t kMinRsLaunchTiles = 2 * kCuTiles;
+// One round: a CU holds at most 7 reduce-scatter workgroups at once (per-tile
+// trace, R = 8..32), so a launch of fewer than 8 per CU starts all of its
+// tiles together and ends with its most loaded CU.  Such launches (4 to 7.x
+// per CU) are rounded to the nearest whole number of workgroups per CU, at
+// most 7: at R = 32 (4.7 per CU at 160 MiB, some CUs holding 5 tiles and
+// the rest 4) 1280 tiles per launch read 6.24 TB/s against 6.04 for 1204
+// (1024: 6.20, 1536: 6.31, 1792: 6.32; same buffers, two processes).
+// Launches of several rounds are left at the byte target: at R = 16, 1792
+// tiles (7 per CU) read +1.1% but 2048 (8) -2.7%, and at R = 8, 3584 (14)
+// -4.5% against 4096 (16), so no simple rule in whole rounds held.
+constexpr int64_t kRsOneRoundTiles = 8 * kCuTiles;
+constexpr int64_t kRsMaxPerCuOneRound = 7;
 constexpr uint32_t kRsLdsReserve = 64 * 1024;
 constexpr int32_t kDefaultAgLaunchMiB = 256;
 
@@ -473,7 +485,10 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
     if (o.rs_launch_bytes > 0) {
         int64_t t = o.rs_launch_bytes / rs_tile_bytes;
-        if (o.rs_round && t < kRsRoundBelowTiles) t = t / kCuTiles * kCuTiles;
+        if (o.rs_round && t < kRsRoundBelowTiles)
+            t = t / kCuTiles * kCuTiles;
+        else if (o.rs_round && t < kRsOneRoundTiles)
+            t = std::min<int64_t>((t + kCuTiles / 2) / kCuTiles, kRsMaxPerCuOneRound) * kCuTiles;
         rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));
     }
     if (o.ag_launch_bytes > 0)

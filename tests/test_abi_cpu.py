@@ -322,12 +322,19 @@ def test_launch_granularity():
     _, i40 = api.tide_desc_build(shapes64, 40, g40, o40, None, None)
     assert (160 << 20) // (i40.rs_tile_elems * (2 * 40 + 4)) == 975
     assert i40.rs_launch_tiles == 768 and i40.rs_lds_bytes == 8192
-    # R = 32: ~1204 tiles per 160 MiB launch, 4.7 per CU, left as is
-    _, _, _, S32 = api.tide_desc_geometry(shapes64, 32)
-    g32, o32, _, _ = _fake_ptrs(shapes64, 32, S32)
-    _, i32 = api.tide_desc_build(shapes64, 32, g32, o32, None, None)
-    assert i32.rs_launch_tiles == (160 << 20) // (i32.rs_tile_elems * (2 * 32 + 4))
-    assert i32.rs_lds_bytes == 8192
+    # one round (4 to 7.x workgroups per CU): rounded to the nearest whole
+    # number per CU, at most 7.  R = 32: ~1204 tiles, 4.7 per CU -> 1280;
+    # R = 24: ~1613, 6.3 -> 1536; R = 20: ~1906, 7.4 -> 1792; R = 16: ~2275,
+    # 8.9 per CU, several rounds: left as is; explicit sizes: not rounded
+    for Rr, want in ((32, 1280), (24, 1536), (20, 1792), (16, (160 << 20) // (2048 * 36))):
+        _, _, _, Sr = api.tide_desc_geometry(shapes64, Rr)
+        gr, orr, _, _ = _fake_ptrs(shapes64, Rr, Sr)
+        _, ir = api.tide_desc_build(shapes64, Rr, gr, orr, None, None)
+        assert ir.rs_tile_elems == 2048
+        assert ir.rs_launch_tiles == min(ir.rs_tiles, want), (Rr, ir.rs_launch_tiles)
+        assert ir.rs_lds_bytes == 8192
+        _, xr = api.tide_desc_build(shapes64, Rr, gr, orr, None, None, launch_mib=160)
+        assert xr.rs_launch_tiles == min(xr.rs_tiles, (160 << 20) // (2048 * (2 * Rr + 4)))
     # a layer of at most 512 tiles is one launch of at most 2 workgroups per
     # CU: reserved too; the host blob carries it and tide_plan_query reads it
     for Rs in (4, 17):
