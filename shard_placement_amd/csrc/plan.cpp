@@ -64,9 +64,10 @@ constexpr int32_t kDefaultFlags = TIDE_FLAG_NT_LOADS | TIDE_FLAG_NT_STORES;
 // LDS) for a workgroup of a concurrent kernel, e.g. the single-wave GEMM's
 // (256 VGPRs per wave, 65 KB of LDS), which then shares the CU with
 // streaming reduce-scatter waves and finishes late.  (Launches of many
-// tiles per CU, as at R = 8, keep 5-6 workgroups of 56 VGPRs resident on
-// every CU for their whole length, per the per-tile trace, which leaves no
-// room for the GEMM's 256-VGPR waves; it waits about half a launch.)  Such
+// tiles per CU, as at R = 8, keep up to 7 workgroups of 38 VGPRs (40
+// allocated) resident on every CU for their whole length, per the per-tile
+// trace: 280 of a SIMD's 512 registers, too few left for the GEMM's
+// 256-VGPR waves; it waits about half a launch.)  Such
 // launches therefore hold 64 KB of LDS per
 // workgroup (the kernel uses 8 KB): two fill 128 of the CU's 160 KB, and a
 // workgroup needing more than 32 KB cannot start beside them.  Measured at

@@ -18,7 +18,7 @@
 // whole compute units at the launch boundaries.  In a vector tile each lane
 // owns 8 consecutive elements: it issues one 16-byte load per rank, a batch
 // of ranks in flight at once (2, 4 or 8 ranks by the rule at pick_fixed:
-// about 32-48 KB of loads in flight per CU), widens bf16 -> fp32 exactly
+// about 32-56 KB of loads in flight per CU), widens bf16 -> fp32 exactly
 // (bits << 16), adds in rank order 0..R-1 starting from rank 0's value (or pairwise, tree
 // order), and hands its 8 results through the wave's own 2 KB of LDS so
 // that each of the wave's two 16-byte-per-lane stores covers one
@@ -592,10 +592,10 @@ RsKernel pick_nt(uint32_t flags) {
 // chunks per lane when R < 8 and the tile holds them, so that up to 8 loads
 // are in flight).  R a multiple of 8 loads 2 ranks per batch, or 4 when the
 // launch holds two workgroups per CU (the plan's LDS reservation): about
-// 32-48 KB of loads in flight per CU read fastest.  Measured on MI355X
+// 32-56 KB of loads in flight per CU read fastest.  Measured on MI355X
 // (same buffers, one process, two processes each): against batches of 8,
 // +1.5..2.1% at R = 8, +1.0..1.6% at R = 16, +1.5..2.3% at R = 32 (2 ranks
-// per batch, 5-6 workgroups per CU) and +1.6..1.9% at R = 64 (4 ranks, 2
+// per batch, up to 7 workgroups per CU) and +1.6..1.9% at R = 64 (4 ranks, 2
 // per CU); 2 ranks at R = 64 read 14% less, 16 ranks 1.5-3.2% less than 8.
 // Any other R batches 8, the last batch re-reading a rank in place of the
 // missing ones.  Chunks per lane for R < 8: as many as the tile holds, up
