@@ -79,17 +79,22 @@ constexpr int32_t kDefaultRsLaunchMiB = 160;
 constexpr int64_t kCuTiles = 256;
 constexpr int64_t kRsRoundBelowTiles = 4 * kCuTiles;
 constexpr int64_t kMinRsLaunchTiles = 2 * kCuTiles;
-// One round: a CU holds at most 7 reduce-scatter workgroups at once (per-tile
-// trace, R = 8..32), so a launch of fewer than 8 per CU starts all of its
-// tiles together and ends with its most loaded CU.  Such launches (4 to 7.x
-// per CU) are rounded to the nearest whole number of workgroups per CU, at
-// most 7: at R = 32 (4.7 per CU at 160 MiB, some CUs holding 5 tiles and
-// the rest 4) 1280 tiles per launch read 6.24 TB/s against 6.04 for 1204
-// (1024: 6.20, 1536: 6.31, 1792: 6.32; same buffers, two processes).
-// Launches of several rounds are left at the byte target: at R = 16, 1792
-// tiles (7 per CU) read +1.1% but 2048 (8) -2.7%, and at R = 8, 3584 (14)
-// -4.5% against 4096 (16), so no simple rule in whole rounds held.
-constexpr int64_t kRsOneRoundTiles = 8 * kCuTiles;
+// One round: a CU holds at most 7 workgroups of the kernel that loads 2
+// ranks per batch (R a multiple of 8; per-tile trace at R = 8, 16 and 32),
+// so a launch of fewer than 8 per CU starts all of its tiles together and
+// ends with its most loaded CU, and one of 8 or a little more ends with a
+// thin second round.  For such R, launches of 4 to 8.x workgroups per CU
+// are rounded to the nearest whole number per CU, at most 7 (same buffers,
+// two processes each): at R = 32, 1280 tiles per launch (5 per CU) read
+// 6.24-6.26 TB/s against 6.04-6.07 for the byte target's 1204 (4.7 per CU;
+// 1024: 6.20, 1536: 6.31, 1792: 6.32); at R = 16, 1792 tiles (7 per CU)
+// read 5.90-5.91 against 5.85 for 2275 (8.9 per CU) on the MoE layer and
+// 5.96-5.98 against 5.87-5.89 on the Llama layer's shapes (2048, 8 per CU:
+// 5.70).  Longer launches keep the byte target (at R = 8, 3584 tiles, 14
+// per CU, read 4.5% less than 4096), and so does the kernel that loads 8
+// ranks per batch (other R), which was not traced (at R = 18, 1792 tiles
+// read 2.5% less than the byte target's 2048).
+constexpr int64_t kRsOneRoundTiles = 9 * kCuTiles;
 constexpr int64_t kRsMaxPerCuOneRound = 7;
 constexpr uint32_t kRsLdsReserve = 64 * 1024;
 constexpr int32_t kDefaultAgLaunchMiB = 256;
@@ -488,7 +493,7 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
         int64_t t = o.rs_launch_bytes / rs_tile_bytes;
         if (o.rs_round && t < kRsRoundBelowTiles)
             t = t / kCuTiles * kCuTiles;
-        else if (o.rs_round && t < kRsOneRoundTiles)
+        else if (o.rs_round && R % 8 == 0 && t < kRsOneRoundTiles)
             t = std::min<int64_t>((t + kCuTiles / 2) / kCuTiles, kRsMaxPerCuOneRound) * kCuTiles;
         rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));
     }

@@ -41,8 +41,10 @@ __device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles) {
 // no tile (-1) and exit; tiles past the last full span take one workgroup
 // each, in order.  Measured against the plain runs (same buffers, one
 // process, interleaved, four processes on three boxes): +0.1..0.8% on the
-// Llama layer (R = 8, 4096 tiles per launch) and +0.8..1.4% on the MoE
-// layer (R = 16, 2275); a skew of 2 read -0.3% / +0.5%.  Launches of about
+// Llama layer (R = 8, 4096 tiles per launch) and +0.4..1.4% on the MoE
+// layer with 2275-tile launches (R = 16; its default launches are now
+// one-round launches of 1792 tiles, plan.cpp); a skew of 2 read -0.3% /
+// +0.5%.  Launches of about
 // one round of workgroups per CU (the R = 32 and R = 64 layers: every tile
 // starts at once) gain nothing, so only launches of kSkewMinTiles or more
 // are skewed.  The kernel reads the skew back from its grid size; the same

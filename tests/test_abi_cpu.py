@@ -322,11 +322,13 @@ def test_launch_granularity():
     _, i40 = api.tide_desc_build(shapes64, 40, g40, o40, None, None)
     assert (160 << 20) // (i40.rs_tile_elems * (2 * 40 + 4)) == 975
     assert i40.rs_launch_tiles == 768 and i40.rs_lds_bytes == 8192
-    # one round (4 to 7.x workgroups per CU): rounded to the nearest whole
-    # number per CU, at most 7.  R = 32: ~1204 tiles, 4.7 per CU -> 1280;
-    # R = 24: ~1613, 6.3 -> 1536; R = 20: ~1906, 7.4 -> 1792; R = 16: ~2275,
-    # 8.9 per CU, several rounds: left as is; explicit sizes: not rounded
-    for Rr, want in ((32, 1280), (24, 1536), (20, 1792), (16, (160 << 20) // (2048 * 36))):
+    # R a multiple of 8, 4 to 8.x workgroups per CU: rounded to the nearest
+    # whole number per CU, at most 7.  R = 32: ~1204 tiles, 4.7 per CU ->
+    # 1280; R = 24: ~1613, 6.3 -> 1536; R = 16: ~2275, 8.9 -> 1792; other R
+    # keep the byte target (R = 20: ~1906, 7.4 per CU; R = 18: 2048);
+    # explicit sizes: not rounded
+    for Rr, want in ((32, 1280), (24, 1536), (16, 1792), (20, (160 << 20) // (2048 * 44)),
+                     (18, (160 << 20) // (2048 * 40))):
         _, _, _, Sr = api.tide_desc_geometry(shapes64, Rr)
         gr, orr, _, _ = _fake_ptrs(shapes64, Rr, Sr)
         _, ir = api.tide_desc_build(shapes64, Rr, gr, orr, None, None)

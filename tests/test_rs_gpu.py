@@ -161,12 +161,13 @@ def test_skewed_launches_bitwise(R):
     """Launches of 2048 tiles or more at R a multiple of 8 (2 ranks per
     batch) run the skewed XCD mapping, in which the odd XCDs' spare
     workgroups take no tile: at R = 8 one skewed launch of 2425 tiles, at
-    R = 16 two of 2275 and a plain one of 299.  Whole arenas against the
+    R = 16 (an explicit 160 MiB: the default makes one-round launches of
+    1792) two of 2275 and a plain one of 299.  Whole arenas against the
     oracle; the per-tile trace stamps every tile exactly once with the same
     bits; a capped grid (no skew) gives the same bits."""
     w = _wl([(300 * R + 3, 2048), (R - 1, 8), (333, 40)], R, key=280 + R, sigma=1e-3)
     gu.say("skewed launches R", R)
-    st = harness.setup(w, with_ag=False)
+    st = harness.setup(w, with_ag=False, launch_mib=160 if R == 16 else 0)
     info = st.plan.info
     assert info.rs_lds_bytes == 8192 and info.rs_launch_tiles >= 2048
     _run(st)
