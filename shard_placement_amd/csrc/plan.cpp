@@ -88,9 +88,10 @@ constexpr int64_t kMinRsLaunchTiles = 2 * kCuTiles;
 // two processes each): at R = 32, 1280 tiles per launch (5 per CU) read
 // 6.24-6.26 TB/s against 6.04-6.07 for the byte target's 1204 (4.7 per CU;
 // 1024: 6.20, 1536: 6.31, 1792: 6.32); at R = 16, 1792 tiles (7 per CU)
-// read 5.90-5.91 against 5.85 for 2275 (8.9 per CU) on the MoE layer and
-// 5.96-5.98 against 5.87-5.89 on the Llama layer's shapes (2048, 8 per CU:
-// 5.70).  Longer launches keep the byte target (at R = 8, 3584 tiles, 14
+// read 5.80-5.91 against 5.70-5.85 for 2275 (8.9 per CU) on the MoE layer
+// (0..+1.7%, four processes) and 5.96-5.98 against 5.87-5.89 on the Llama
+// layer's shapes (2048, 8 per CU: 5.70), with the GEMM beside the MoE layer
+// at +2.9..5.7% against +4.1..8.1%.  Longer launches keep the byte target (at R = 8, 3584 tiles, 14
 // per CU, read 4.5% less than 4096), and so does the kernel that loads 8
 // ranks per batch (other R), which was not traced (at R = 18, 1792 tiles
 // read 2.5% less than the byte target's 2048).
