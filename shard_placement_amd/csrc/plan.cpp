@@ -490,11 +490,16 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     const int64_t ag_tile_bytes = (int64_t)o.ag_tile * 4;
     int64_t rs_launch = std::max<int64_t>(1, (int64_t)rs.size());
     int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
+    // the tree-order kernels hold more registers and were not traced: their
+    // launches keep the byte target (with the one-round sizes of the
+    // fixed-order kernel they read 0.8-1.8% less on the R = 16 and R = 32
+    // layers)
+    int64_t rs_launch_tree = rs_launch;
     if (o.rs_launch_bytes > 0) {
         int64_t t = o.rs_launch_bytes / rs_tile_bytes;
-        if (o.rs_round && t < kRsRoundBelowTiles)
-            t = t / kCuTiles * kCuTiles;
-        else if (o.rs_round && R % 8 == 0 && t < kRsOneRoundTiles)
+        if (o.rs_round && t < kRsRoundBelowTiles) t = t / kCuTiles * kCuTiles;
+        rs_launch_tree = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));
+        if (o.rs_round && R % 8 == 0 && t >= kRsRoundBelowTiles && t < kRsOneRoundTiles)
             t = std::min<int64_t>((t + kCuTiles / 2) / kCuTiles, kRsMaxPerCuOneRound) * kCuTiles;
         rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));
     }
@@ -548,6 +553,7 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     h.flags = o.flags;
     h.rs_launch_tiles = rs_launch;
     h.ag_launch_tiles = ag_launch;
+    h.rs_launch_tiles_tree = rs_launch_tree;
     h.rs_lds_bytes = rs_lds;
     std::memcpy(b, &h, sizeof h);
     if (P) std::memcpy(b + L.off_params, ps.data(), sizeof(ParamDesc) * (size_t)P);

@@ -15,7 +15,7 @@
 namespace tide {
 
 constexpr uint32_t kMagic = 0x45444954u;  // "TIDE"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 constexpr int kBlock = 256;        // threads per workgroup (4 wave64)
 constexpr int kVec = 8;            // bf16 elements per 16-byte vector
 constexpr int kTileQuantum = kBlock * kVec;  // tile sizes are multiples of this
@@ -55,6 +55,7 @@ struct PlanHeader {
     uint32_t rs_lds_bytes;    // LDS per reduce-scatter workgroup (0: the kernels' own)
     int64_t rs_launch_tiles;  // tiles per reduce-scatter kernel launch
     int64_t ag_launch_tiles;  // tiles per placement kernel launch
+    int64_t rs_launch_tiles_tree;  // the same for the tree-order kernels
 };
 
 struct ParamDesc {

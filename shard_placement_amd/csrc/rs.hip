@@ -748,7 +748,8 @@ tide_status launch_rs(const void* h_plan, const void* d_plan, int32_t order, int
     RsKernel ks = order == 0 && max_workgroups == 0
                       ? pick_fixed_skewed(R, h.flags, holds_two_per_cu(h))
                       : nullptr;
-    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : tile_count;
+    const int64_t launch_tiles = order == 1 ? h.rs_launch_tiles_tree : h.rs_launch_tiles;
+    const int64_t per_launch = launch_tiles > 0 ? launch_tiles : tile_count;
 
     // One launch per run of per_launch tiles: the launch boundaries are where
     // kernels on other hardware queues get whole compute units.
@@ -826,7 +827,8 @@ extern "C" tide_status tide_rs_fold_staged(const void* h_plan, const void* d_pla
     int64_t stride = 2 * slot_stride;
     FoldKernel k = order == 0 ? pick_fold(R, h.flags, h.rs_tile, holds_two_per_cu(h))
                               : pick_fold_tree(R, h.flags);
-    const int64_t per_launch = h.rs_launch_tiles > 0 ? h.rs_launch_tiles : h.n_rs_tiles;
+    const int64_t launch_tiles = order == 1 ? h.rs_launch_tiles_tree : h.rs_launch_tiles;
+    const int64_t per_launch = launch_tiles > 0 ? launch_tiles : h.n_rs_tiles;
     for (int64_t b = 0; b < h.n_rs_tiles; b += per_launch) {
         const RsTile* tiles = all + b;
         int64_t ntiles = per_launch < h.n_rs_tiles - b ? per_launch : h.n_rs_tiles - b;

@@ -22,7 +22,8 @@ HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("R", "<i4"), ("P", "<i4")
                 ("off_params", "<u8"), ("off_gptr", "<u8"), ("off_obase", "<u8"),
                 ("off_full", "<u8"), ("off_rs", "<u8"), ("off_ag", "<u8"),
                 ("gathered", "<u8"), ("bytes", "<u8"), ("has_rs", "<i4"), ("has_ag", "<i4"),
-                ("flags", "<u4"), ("reserved", "<u4"), ("rs_launch", "<i8"), ("ag_launch", "<i8")])
+                ("flags", "<u4"), ("reserved", "<u4"), ("rs_launch", "<i8"), ("ag_launch", "<i8"),
+                ("rs_launch_tree", "<i8")])
 RS_TILE = np.dtype([("j0", "<i8"), ("o0", "<i8"), ("p", "<i4"), ("r", "<i4"),
                     ("len", "<i4"), ("kind", "<i4")])
 AG_TILE = np.dtype([("src", "<i8"), ("dst", "<i8"), ("p", "<i4"), ("len", "<i4"),
@@ -331,9 +332,13 @@ def test_launch_granularity():
                      (18, (160 << 20) // (2048 * 40))):
         _, _, _, Sr = api.tide_desc_geometry(shapes64, Rr)
         gr, orr, _, _ = _fake_ptrs(shapes64, Rr, Sr)
-        _, ir = api.tide_desc_build(shapes64, Rr, gr, orr, None, None)
+        blob_r, ir = api.tide_desc_build(shapes64, Rr, gr, orr, None, None)
         assert ir.rs_tile_elems == 2048
         assert ir.rs_launch_tiles == min(ir.rs_tiles, want), (Rr, ir.rs_launch_tiles)
+        # the tree-order launches keep the byte target
+        hr = decode(blob_r)[0]
+        assert hr["rs_launch"] == ir.rs_launch_tiles
+        assert hr["rs_launch_tree"] == min(ir.rs_tiles, (160 << 20) // (2048 * (2 * Rr + 4)))
         assert ir.rs_lds_bytes == 8192
         _, xr = api.tide_desc_build(shapes64, Rr, gr, orr, None, None, launch_mib=160)
         assert xr.rs_launch_tiles == min(xr.rs_tiles, (160 << 20) // (2048 * (2 * Rr + 4)))
