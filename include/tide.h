@@ -106,7 +106,11 @@ typedef struct tide_opts {
                               the launch boundaries (0: defaults, 160 MiB for the
                               reduce-scatter, rounded down to a multiple of 256
                               tiles (one per CU) when it holds fewer than 1024,
-                              and at least 512 tiles; 256 MiB for the placement;
+                              and at least 512 tiles; for R a multiple of 8 and
+                              1024 to 2303 tiles, the fixed order's launches take
+                              the nearest whole number of tiles per CU, at most 7
+                              (one round of workgroups), while the tree order's
+                              keep the byte target; 256 MiB for the placement;
                               -1: one launch; an explicit size is not rounded) */
 } tide_opts;
 
@@ -124,7 +128,7 @@ typedef struct tide_plan_info {
     int64_t ag_tiles;       /* 0 when the plan has no placement pointers */
     int32_t rs_tile_elems, ag_tile_elems;
     int64_t blob_bytes;     /* bytes of the blob in use: upload this many */
-    int64_t rs_launch_tiles; /* tiles per reduce-scatter launch */
+    int64_t rs_launch_tiles; /* tiles per reduce-scatter launch (fixed order) */
     int64_t ag_launch_tiles; /* tiles per placement launch */
     int64_t rs_lds_bytes;    /* LDS each reduce-scatter workgroup holds: 8 KB (what
                                 the kernels use), or 64 KB when a default launch
