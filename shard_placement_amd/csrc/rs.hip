@@ -14,17 +14,18 @@
 // strides over tiles when the grid is capped), runs of 32 consecutive tiles
 // going to one XCD (runs of 33 and 31 tiles on even and odd XCDs in long
 // launches: xcd_map.h).  A call is cut into launches of about 160 MiB of
-// traffic (the plan's launch size) so that kernels on other queues get
-// whole compute units at the launch boundaries.  In a vector tile each lane
-// owns 8 consecutive elements: it issues one 16-byte load per rank, a batch
-// of ranks in flight at once (2, 4 or 8 ranks by the rule at pick_fixed:
-// about 32-56 KB of loads in flight per CU), widens bf16 -> fp32 exactly
-// (bits << 16), adds in rank order 0..R-1 starting from rank 0's value (or pairwise, tree
-// order), and hands its 8 results through the wave's own 2 KB of LDS so
-// that each of the wave's two 16-byte-per-lane stores covers one
-// contiguous 1 KB run.  Padding tiles only write +0.0f.  There is no
-// inter-workgroup communication.  The path is HBM-bound (about 0.25-0.5
-// flop per byte), so there is no MFMA here.
+// traffic (the plan's launch size) so that kernels on other queues get whole
+// compute units at the launch boundaries.  In a vector tile each lane owns 8
+// consecutive elements: it issues one 16-byte load per rank, a batch of
+// ranks in flight at once (2, 4 or 8 ranks by the rule at pick_fixed: about
+// 32-56 KB of loads in flight per CU), widens bf16 -> fp32 exactly
+// (bits << 16), adds in rank order 0..R-1 starting from rank 0's value (or
+// pairwise, tree order), and hands its 8 results through the wave's own 2 KB
+// of LDS so
+// that each of the wave's two 16-byte-per-lane stores covers one contiguous
+// 1 KB run.  Padding tiles only write +0.0f.  There is no inter-workgroup
+// communication.  The path is HBM-bound (about 0.25-0.5 flop per byte), so
+// there is no MFMA here.
 #include <hip/hip_runtime.h>
 
 #include <climits>
