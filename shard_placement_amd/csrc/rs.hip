@@ -21,11 +21,10 @@
 // 32-56 KB of loads in flight per CU), widens bf16 -> fp32 exactly
 // (bits << 16), adds in rank order 0..R-1 starting from rank 0's value (or
 // pairwise, tree order), and hands its 8 results through the wave's own 2 KB
-// of LDS so
-// that each of the wave's two 16-byte-per-lane stores covers one contiguous
-// 1 KB run.  Padding tiles only write +0.0f.  There is no inter-workgroup
-// communication.  The path is HBM-bound (about 0.25-0.5 flop per byte), so
-// there is no MFMA here.
+// of LDS so that each of the wave's two 16-byte-per-lane stores covers one
+// contiguous 1 KB run.  Padding tiles only write +0.0f.  There is no
+// inter-workgroup communication.  The path is HBM-bound (about 0.25-0.5 flop
+// per byte), so there is no MFMA here.
 #include <hip/hip_runtime.h>
 
 #include <climits>
