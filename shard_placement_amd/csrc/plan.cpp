@@ -490,8 +490,8 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     const int64_t ag_tile_bytes = (int64_t)o.ag_tile * 4;
     int64_t rs_launch = std::max<int64_t>(1, (int64_t)rs.size());
     int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
-    // the tree-order kernels hold more registers and were not traced: their
-    // launches keep the byte target (with the one-round sizes of the
+    // the tree-order kernels hold 109 VGPRs (at most 4 workgroups per CU):
+    // their launches keep the byte target (with the one-round sizes of the
     // fixed-order kernel they read 0.8-1.8% less on the R = 16 and R = 32
     // layers)
     int64_t rs_launch_tree = rs_launch;
