@@ -490,15 +490,22 @@ tide_status tide_desc_build(const tide_shape* shapes, int32_t P, int32_t R, cons
     const int64_t ag_tile_bytes = (int64_t)o.ag_tile * 4;
     int64_t rs_launch = std::max<int64_t>(1, (int64_t)rs.size());
     int64_t ag_launch = std::max<int64_t>(1, (int64_t)ag.size());
-    // the tree-order kernels hold 109 VGPRs (at most 4 workgroups per CU):
-    // their launches keep the byte target (with the one-round sizes of the
-    // fixed-order kernel they read 0.8-1.8% less on the R = 16 and R = 32
-    // layers)
+    // The tree-order kernels hold 109 VGPRs, so at most 4 of their
+    // workgroups fit on a CU: with the fixed order's one-round sizes they
+    // read 0.8-1.8% less on the R = 16 and R = 32 layers.  Their launches of
+    // 4 to 8.x workgroups per CU (R a multiple of 8) are rounded down to
+    // whole rounds of 4 per CU instead: the DiT block (R = 32) 1024 tiles
+    // against the byte target's 1204, 5.85-5.86 TB/s against 5.75-5.76; the
+    // MoE layer (R = 16) 2048 against 2275, 5.70-5.71 against 5.69-5.70 (same
+    // buffers, two processes).
     int64_t rs_launch_tree = rs_launch;
     if (o.rs_launch_bytes > 0) {
         int64_t t = o.rs_launch_bytes / rs_tile_bytes;
         if (o.rs_round && t < kRsRoundBelowTiles) t = t / kCuTiles * kCuTiles;
-        rs_launch_tree = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));
+        int64_t tt = t;
+        if (o.rs_round && R % 8 == 0 && t >= kRsRoundBelowTiles && t < kRsOneRoundTiles)
+            tt = t / kRsRoundBelowTiles * kRsRoundBelowTiles;
+        rs_launch_tree = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, tt));
         if (o.rs_round && R % 8 == 0 && t >= kRsRoundBelowTiles && t < kRsOneRoundTiles)
             t = std::min<int64_t>((t + kCuTiles / 2) / kCuTiles, kRsMaxPerCuOneRound) * kCuTiles;
         rs_launch = std::min(rs_launch, std::max<int64_t>(o.rs_min_tiles, t));

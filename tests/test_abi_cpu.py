@@ -335,10 +335,13 @@ def test_launch_granularity():
         blob_r, ir = api.tide_desc_build(shapes64, Rr, gr, orr, None, None)
         assert ir.rs_tile_elems == 2048
         assert ir.rs_launch_tiles == min(ir.rs_tiles, want), (Rr, ir.rs_launch_tiles)
-        # the tree-order launches keep the byte target
+        # the tree-order launches: whole rounds of 4 per CU for R a multiple
+        # of 8 (R = 32: 1024, R = 24: 1024, R = 16: 2048), else the byte target
         hr = decode(blob_r)[0]
         assert hr["rs_launch"] == ir.rs_launch_tiles
-        assert hr["rs_launch_tree"] == min(ir.rs_tiles, (160 << 20) // (2048 * (2 * Rr + 4)))
+        target = (160 << 20) // (2048 * (2 * Rr + 4))
+        want_tree = target // 1024 * 1024 if Rr % 8 == 0 else target
+        assert hr["rs_launch_tree"] == min(ir.rs_tiles, want_tree), (Rr, hr["rs_launch_tree"])
         assert ir.rs_lds_bytes == 8192
         _, xr = api.tide_desc_build(shapes64, Rr, gr, orr, None, None, launch_mib=160)
         assert xr.rs_launch_tiles == min(xr.rs_tiles, (160 << 20) // (2048 * (2 * Rr + 4)))
