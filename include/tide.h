@@ -109,8 +109,9 @@ typedef struct tide_opts {
                               and at least 512 tiles; for R a multiple of 8 and
                               1024 to 2303 tiles, the fixed order's launches take
                               the nearest whole number of tiles per CU, at most 7
-                              (one round of workgroups), while the tree order's
-                              keep the byte target; 256 MiB for the placement;
+                              (one round of workgroups), and the tree order's
+                              whole rounds of 4 per CU (4 or 8); 256 MiB for
+                              the placement;
                               -1: one launch; an explicit size is not rounded) */
 } tide_opts;
 
