@@ -272,6 +272,14 @@ def test_launches_reject_before_touching_the_gpu():
     assert L.tide_plan_query(junk.ctypes.data, ctypes.byref(info)) == -7
     assert L.tide_plan_query(blob.ctypes.data, ctypes.byref(info)) == 0
     assert info.R == R and info.slot_numel == S
+    # a blob of another format version (here the previous one, without the
+    # tree-order launch size) is refused, not misread
+    old = blob.copy()
+    hv = np.frombuffer(old[:HDR.itemsize].tobytes(), HDR)[0]
+    assert hv["version"] == 2
+    old[4:8] = np.frombuffer(np.uint32(1).tobytes(), np.uint8)
+    assert L.tide_plan_query(old.ctypes.data, ctypes.byref(info)) == -7
+    assert L.tide_rs_bf16_to_fp32(old.ctypes.data, fake_dev, 0, 0, None) == -7
     n_rs = int(np.frombuffer(blob[:HDR.itemsize].tobytes(), HDR)[0]["n_rs"])
     T = L.tide_rs_bf16_to_fp32_tiles
     assert T(blob.ctypes.data, fake_dev, 0, 0, n_rs + 1, 0, None) == -1          # past the end
