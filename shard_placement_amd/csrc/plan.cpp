@@ -79,13 +79,14 @@ constexpr int32_t kDefaultRsLaunchMiB = 160;
 constexpr int64_t kCuTiles = 256;
 constexpr int64_t kRsRoundBelowTiles = 4 * kCuTiles;
 constexpr int64_t kMinRsLaunchTiles = 2 * kCuTiles;
-// One round: a CU holds at most 7 workgroups of the kernel that loads 2
-// ranks per batch (R a multiple of 8; per-tile trace at R = 8, 16 and 32),
-// so a launch of fewer than 8 per CU starts all of its tiles together and
-// ends with its most loaded CU, and one of 8 or a little more ends with a
-// thin second round.  For such R, launches of 4 to 8.x workgroups per CU
-// are rounded to the nearest whole number per CU, at most 7 (same buffers,
-// two processes each): at R = 32, 1280 tiles per launch (5 per CU) read
+// One round: a CU holds up to 8 workgroups of the kernel that loads 2 ranks
+// per batch (R a multiple of 8), 7 of its skewed form (per-tile trace at
+// R = 8, 16 and 32), so a launch of up to 7 per CU starts all of its tiles
+// together and ends with its most loaded CU, and a longer one of 8.x ends
+// with a thin second round.  For such R, launches of 4 to 8.x workgroups
+// per CU are rounded to the nearest whole number per CU, at most 7 (one
+// round for either form; 8 per CU with the plain form read 0.5% less than
+// 7 on the MoE layer) (same buffers, two processes each): at R = 32, 1280 tiles per launch (5 per CU) read
 // 6.24-6.26 TB/s against 6.04-6.07 for the byte target's 1204 (4.7 per CU;
 // 1024: 6.20, 1536: 6.31, 1792: 6.32); at R = 16, 1792 tiles (7 per CU)
 // read 5.80-5.91 against 5.70-5.85 for 2275 (8.9 per CU) on the MoE layer
