@@ -50,7 +50,9 @@ __device__ __forceinline__ int64_t tile_of(int64_t b, int64_t ntiles) {
 // are skewed.  The kernel reads the skew back from its grid size; the same
 // mapping with the skew as a compile-time constant read 0.5-1% slower (the
 // compiler's code for the tile loop differs), and so did the plain launches
-// when they ran this form.
+// when they ran this form.  This form holds at most 7 workgroups per CU
+// (92 scalar registers) where the plain one holds 8; holding plain launches
+// to 7 per CU through LDS did not reproduce the gain.
 constexpr int kXcdSkew = 1;
 constexpr int64_t kSkewMinTiles = 8 * kXcdSpan;
 
