@@ -46,6 +46,21 @@ def decode(blob):
     return h, ps, gp, rs, ag
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/tide.h compiles on its own as C99 and as C++11, warnings as
+    errors: a C ABI with no HIP, torch or C++ types in its signatures."""
+    import shutil
+    import subprocess
+
+    for cc, std, ext in (("gcc", "-std=c99", "c"), ("g++", "-std=c++11", "cpp")):
+        if shutil.which(cc) is None:
+            pytest.skip("%s not available" % cc)
+        src = tmp_path / ("use_header." + ext)
+        src.write_text('#include "tide.h"\nint main(void) { return (int)TIDE_OK; }\n')
+        subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I" + os.path.join(ROOT, "include"), str(src)], check=True)
+
+
 def test_library_loads_and_exports_header_symbols():
     with open(os.path.join(ROOT, "include", "tide.h")) as fh:
         hdr = fh.read()
